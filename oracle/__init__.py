@@ -1,0 +1,57 @@
+"""fp64 CPU oracle for the FlashAttention forward pass.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this package.
+The library (``flashattention_forward_02_amd``) never imports it, and this package
+imports nothing from the library: the two share no code. Inputs come from
+``seeded_inputs`` (random draws and storage formats only).
+
+Sources, cited by tag and section throughout:
+
+* [FA-Simplified] "FlashAttention 简化版：Tiling + Online Softmax"
+  (forceinjection.github.io, 02_npu_programming/09_flash_attention).
+* [FA-Fill] "Flash Attention 代码填空 (Level 2-3)" (boots-coder.github.io, LLM-101-CN).
+* [CS349E-L11] "CS349E 第 11 讲 01_online_softmax.py" (semidirectx.com, cs349e/code/lecture11).
+* [FA-Scratch] "从零手写 FlashAttention（PyTorch实现 + 原理推导）" (mokono.cn, news/2160643).
+
+What each function is pinned against (tests/test_oracle_pins.py):
+
+* ``attention_fp64`` -- brute force in pure Python on tiny inputs; torch's
+  float64 scaled-dot-product attention and scipy's softmax; closed forms (one key,
+  constant V, zero scale, two keys, V = I); shift and joint-permutation
+  invariance; the one-pass recurrence at the pages' demo size.
+* ``online_softmax`` / ``safe_softmax`` -- scipy's softmax; overflow-free on
+  shifted inputs where the naive form overflows.
+* ``online_attention`` / ``online_attention_row`` -- the three-pass definition at
+  the 1e-16 level the lecture-11 demo 1 reports.
+* ``partial_state`` / ``merge_states`` / ``merge_*`` -- order independence at the
+  1e-16 level the lecture-11 demo 2 reports, on the demo's own draws; empty states.
+* ``fa1_order_attention`` -- the delayed-normalisation form.
+* ``round_to_bf16`` / ``round_to_f16`` -- torch's and numpy's casts; the
+  relative P.V error magnitudes the lecture-11 demo 4 reports.
+
+Parity unpinned: nothing in this package. (The exact bf16 error of a GPU kernel
+depends on where its tiles fall and is bounded by the tolerance, not pinned.)
+"""
+from .attention import (  # noqa: F401
+    scores_fp64,
+    attention_fp64,
+    attention_rows_fp64,
+    safe_softmax,
+    naive_softmax,
+    online_softmax,
+    online_attention_row,
+    two_pass_attention_row,
+    online_attention,
+    fa1_order_attention,
+    partial_state,
+    merge_states,
+    merge_sequential,
+    merge_tree,
+    finish_state,
+    split_bounds,
+    split_partial_states,
+    brute_force_attention,
+    round_to_bf16,
+    round_to_f16,
+)

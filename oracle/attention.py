@@ -1,0 +1,391 @@
+"""Plain, slow, float64 attention and online-softmax reference (test infrastructure only).
+
+See the package docstring for the source tags ([FA-Simplified], [FA-Fill],
+[CS349E-L11], [FA-Scratch]) and what pins each function.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ---------------------------------------------------------------------------
+# The definition: three passes over each score row
+# ---------------------------------------------------------------------------
+
+def scores_fp64(q, k, scale) -> np.ndarray:
+    """s[i, j] = scale * sum_c q[i, c] * k[j, c], in float64.
+
+    [FA-Simplified §1.1] and [FA-Fill Exercise 1]: S = Q K^T / sqrt(d); the scale
+    is applied before the maximum is taken. ``scale`` is taken as given (callers
+    pass the float32 value the GPU receives); [FA-Scratch §1] is the case scale = 1.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    return float(scale) * (q @ k.T)
+
+
+def attention_rows_fp64(q, k, v, scale):
+    """Full attention for one head: q [Nq, d], k [Nk, d], v [Nk, dv] -> (O [Nq, dv], m [Nq], l [Nq]).
+
+    The three passes of the stored-row form ([CS349E-L11] ``attn_row_3pass``;
+    [FA-Simplified §2.1]): m = max_j s_j; p_j = exp(s_j - m), l = sum_j p_j;
+    O = (sum_j p_j v_j) / l. ``m`` is the row maximum of the scaled scores and
+    ``l`` the sum of exp(s_j - m) (the statistics [FA-Fill Exercise 5] keeps for
+    the backward pass).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k.shape[0] < 1:
+        raise ValueError("softmax over an empty key set is undefined (Nk must be >= 1)")
+    s = scores_fp64(q, k, scale)                 # pass 0: the whole score row is stored
+    m = s.max(axis=1)                            # pass 1: row maximum
+    p = np.exp(s - m[:, None])                   # pass 2: exponentials and their sum
+    l = p.sum(axis=1)
+    o = (p @ v) / l[:, None]                     # pass 3: normalise and weight V
+    return o, m, l
+
+
+def attention_fp64(q, k, v, scale, row_block: int = 512, return_stats: bool = False):
+    """O = softmax(scale * Q K^T) V for [B, H, Nq, d] / [B, H, Nk, d] inputs (or any leading dims).
+
+    The result every kernel must reproduce ([FA-Simplified §3.1]: tiling does the
+    same arithmetic as standard attention, only its rounding order differs;
+    [FA-Simplified §4.1]). Rows are processed in blocks of ``row_block`` queries
+    so no buffer exceeds [row_block, Nk] float64; that is a memory bound on this
+    reference only and changes no arithmetic.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    assert k.shape[:-2] == lead and v.shape[:-2] == lead, "Q, K, V leading dims differ"
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    qf = q.reshape(-1, Nq, q.shape[-1])
+    kf = k.reshape(-1, Nk, k.shape[-1])
+    vf = v.reshape(-1, Nk, v.shape[-1])
+    out = np.empty((qf.shape[0], Nq, vf.shape[-1]))
+    ms = np.empty((qf.shape[0], Nq))
+    ls = np.empty((qf.shape[0], Nq))
+    for h in range(qf.shape[0]):
+        for r0 in range(0, Nq, row_block):
+            o, m, l = attention_rows_fp64(qf[h, r0:r0 + row_block], kf[h], vf[h], scale)
+            out[h, r0:r0 + row_block] = o
+            ms[h, r0:r0 + row_block] = m
+            ls[h, r0:r0 + row_block] = l
+    out = out.reshape(lead + (Nq, vf.shape[-1]))
+    if return_stats:
+        return out, ms.reshape(lead + (Nq,)), ls.reshape(lead + (Nq,))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Softmax forms
+# ---------------------------------------------------------------------------
+
+def naive_softmax(x) -> np.ndarray:
+    """exp(x_i) / sum_j exp(x_j) without the shift: overflows for large x ([FA-Fill Exercise 2])."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(x)
+        return e / e.sum(axis=-1, keepdims=True)
+
+
+def safe_softmax(x) -> np.ndarray:
+    """Two-pass stable softmax: subtract the row maximum, exponentiate, divide by the sum.
+
+    [FA-Simplified §2.1]; [FA-Fill Exercise 2]; [FA-Scratch §3].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max(axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def online_softmax(x) -> np.ndarray:
+    """Element-at-a-time online softmax over the last axis, in plain Python floats.
+
+    [FA-Fill Exercise 2]: while scanning a row keep the running maximum m and the
+    running sum l of exp(x - m); when x_j raises the maximum, the old sum is
+    scaled by exp(m_old - m_new) before exp(x_j - m_new) is added. A second scan
+    writes exp(x_j - m) / l. For small inputs only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty_like(flat)
+    for r, row in enumerate(flat):
+        m, l = NEG_INF, 0.0
+        for xj in row:
+            xj = float(xj)
+            m_next = max(m, xj)
+            l = l * math.exp(m - m_next) + math.exp(xj - m_next)
+            m = m_next
+        for j, xj in enumerate(row):
+            out[r, j] = math.exp(float(xj) - m) / l
+    return out.reshape(x.shape)
+
+
+# ---------------------------------------------------------------------------
+# The one-pass (m, l, acc) recurrence
+# ---------------------------------------------------------------------------
+
+def online_attention_row(q, K, V, block: int, scale=None, trace=None) -> np.ndarray:
+    """One query against all keys in a single pass, ``block`` keys at a time.
+
+    [CS349E-L11] ``attn_row_1pass`` / demo 1; [FA-Simplified §2.3]: the state is
+    the running maximum m (starts at -inf), the running sum l (0) and the
+    accumulator acc (0, length dv). For each block of scores s:
+    m' = max(m, max s); alpha = exp(m - m') (0 on the first block);
+    l = alpha*l + sum exp(s - m'); acc = alpha*acc + exp(s - m') V_block; m = m'.
+    The answer is acc / l. Ragged last blocks are taken as they come. When
+    ``trace`` is a list, (block index, block max, m', alpha, l) is appended per
+    block (the table the demo prints).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[0])
+    m, l = NEG_INF, 0.0
+    acc = np.zeros(V.shape[1])
+    for b, start in enumerate(range(0, K.shape[0], block)):
+        s = float(scale) * (K[start:start + block] @ q)
+        m_next = max(m, float(s.max()))
+        alpha = math.exp(m - m_next)
+        p = np.exp(s - m_next)
+        l = alpha * l + float(p.sum())
+        acc = alpha * acc + p @ V[start:start + block]
+        if trace is not None:
+            trace.append((b, float(s.max()), m_next, alpha, l))
+        m = m_next
+    return acc / l
+
+
+def two_pass_attention_row(q, K, V, block: int, scale=None) -> np.ndarray:
+    """[CS349E-L11] ``attn_row_2pass``: one scan for (m, l), a second scan recomputing the scores for sum p V / l."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[0])
+    m, l = NEG_INF, 0.0
+    for start in range(0, K.shape[0], block):
+        s = float(scale) * (K[start:start + block] @ q)
+        m_next = max(m, float(s.max()))
+        l = l * math.exp(m - m_next) + float(np.exp(s - m_next).sum())
+        m = m_next
+    out = np.zeros(V.shape[1])
+    for start in range(0, K.shape[0], block):
+        s = float(scale) * (K[start:start + block] @ q)
+        out += (np.exp(s - m) / l) @ V[start:start + block]
+    return out
+
+
+def online_attention(q, k, v, scale, Br: int, Bc: int, return_stats: bool = False):
+    """Tiled forward, Q tiles outside and K/V tiles inside, normalised once at the end.
+
+    [FA-Simplified §2.3 and §3.1]; [FA-Scratch §4-§5]. For each Q tile of Br rows
+    the state (m, l, O) is reset to (-inf, 0, 0); for each K/V tile of Bc keys:
+    S = scale Q_i K_j^T; m' = max(m, rowmax S); c = exp(m - m');
+    P = exp(S - m'); l = c l + rowsum P; O = c O + P V_j; m = m'. After the last
+    tile O / l is written. Tails shorter than Br or Bc are processed as shorter
+    tiles. Works on [..., N, d] inputs, one head at a time.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    qf = q.reshape(-1, Nq, q.shape[-1])
+    kf = k.reshape(-1, Nk, k.shape[-1])
+    vf = v.reshape(-1, Nk, v.shape[-1])
+    out = np.empty((qf.shape[0], Nq, vf.shape[-1]))
+    ms = np.empty((qf.shape[0], Nq))
+    ls = np.empty((qf.shape[0], Nq))
+    for h in range(qf.shape[0]):
+        for i0 in range(0, Nq, Br):
+            Qi = qf[h, i0:i0 + Br]
+            m = np.full(Qi.shape[0], NEG_INF)
+            l = np.zeros(Qi.shape[0])
+            O = np.zeros((Qi.shape[0], vf.shape[-1]))
+            for j0 in range(0, Nk, Bc):
+                S = float(scale) * (Qi @ kf[h, j0:j0 + Bc].T)
+                m_next = np.maximum(m, S.max(axis=1))
+                c = np.exp(m - m_next)
+                P = np.exp(S - m_next[:, None])
+                l = c * l + P.sum(axis=1)
+                O = c[:, None] * O + P @ vf[h, j0:j0 + Bc]
+                m = m_next
+            out[h, i0:i0 + Br] = O / l[:, None]
+            ms[h, i0:i0 + Br] = m
+            ls[h, i0:i0 + Br] = l
+    out = out.reshape(lead + (Nq, vf.shape[-1]))
+    if return_stats:
+        return out, ms.reshape(lead + (Nq,)), ls.reshape(lead + (Nq,))
+    return out
+
+
+def fa1_order_attention(q, k, v, scale, block: int) -> np.ndarray:
+    """The K/V-outer, Q-inner order that renormalises O at every step ([FA-Fill Exercise 4]).
+
+    For each K/V block j, for each Q block i: S = scale Q_i K_j^T; m' = max(m_i, rowmax S);
+    P = exp(S - m'); l' = l_i exp(m_i - m') + rowsum P;
+    O_i = O_i (l_i exp(m_i - m') / l') + (P V_j) / l'; then l_i = l', m_i = m'.
+    O is normalised at every step, so nothing is divided at the end. Single head [N, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Nq, Nk = q.shape[0], k.shape[0]
+    O = np.zeros((Nq, v.shape[1]))
+    l = np.zeros(Nq)
+    m = np.full(Nq, NEG_INF)
+    for j0 in range(0, Nk, block):
+        Kj, Vj = k[j0:j0 + block], v[j0:j0 + block]
+        for i0 in range(0, Nq, block):
+            rows = slice(i0, i0 + block)
+            S = float(scale) * (q[rows] @ Kj.T)
+            m_next = np.maximum(m[rows], S.max(axis=1))
+            P = np.exp(S - m_next[:, None])
+            carried = l[rows] * np.exp(m[rows] - m_next)
+            l_next = carried + P.sum(axis=1)
+            O[rows] = O[rows] * (carried / l_next)[:, None] + (P @ Vj) / l_next[:, None]
+            l[rows] = l_next
+            m[rows] = m_next
+    return O
+
+
+# ---------------------------------------------------------------------------
+# Partial states and their merge (split-KV)
+# ---------------------------------------------------------------------------
+
+def partial_state(s, V):
+    """(m, l, o) of one segment of score rows: m = max s, l = sum exp(s - m), o = sum exp(s - m) v (unnormalised).
+
+    [CS349E-L11] demo 2 builds these per segment and finishes a state as o / l,
+    which fixes o as the unnormalised weighted sum. ``s`` is [rows, n], V [n, dv].
+    An empty segment (n = 0) is the identity state (-inf, 0, 0).
+    """
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    V = np.asarray(V, dtype=np.float64)
+    if s.shape[1] == 0:
+        return (np.full(s.shape[0], NEG_INF), np.zeros(s.shape[0]), np.zeros((s.shape[0], V.shape[1])))
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return m, p.sum(axis=1), p @ V
+
+
+def _weight(m_part, m_total):
+    """exp(m_part - m_total), with 0 for an empty part (m_part = -inf) so that -inf - (-inf) never occurs."""
+    m_part = np.asarray(m_part, dtype=np.float64)
+    w = np.zeros_like(m_part)
+    live = np.isfinite(m_part)
+    w[live] = np.exp(m_part[live] - np.asarray(m_total, dtype=np.float64)[live])
+    return w
+
+
+def merge_states(a, b):
+    """Combine two partial states of disjoint key sets into the state of their union.
+
+    The merge [CS349E-L11] demo 2 uses but does not print, derived from the
+    recurrence of [FA-Scratch §4] and the two-block identity of [FA-Simplified §2.2]:
+    m = max(m_a, m_b); l = l_a e^(m_a-m) + l_b e^(m_b-m); o = o_a e^(m_a-m) + o_b e^(m_b-m).
+    A part whose m is -inf (no keys) contributes weight 0.
+    """
+    ma, la, oa = a
+    mb, lb, ob = b
+    m = np.maximum(ma, mb)
+    wa, wb = _weight(ma, m), _weight(mb, m)
+    return m, la * wa + lb * wb, oa * wa[..., None] + ob * wb[..., None]
+
+
+def merge_sequential(states, order=None):
+    """Fold states left to right, in ``order`` (a permutation of their indices) when given ([CS349E-L11] demo 2)."""
+    idx = list(range(len(states))) if order is None else [int(i) for i in order]
+    acc = states[idx[0]]
+    for i in idx[1:]:
+        acc = merge_states(acc, states[i])
+    return acc
+
+
+def merge_tree(states):
+    """Pairwise (tree) merge, as a parallel reduction would do it ([CS349E-L11] demo 2)."""
+    level = list(states)
+    while len(level) > 1:
+        nxt = []
+        for i in range(0, len(level), 2):
+            nxt.append(merge_states(level[i], level[i + 1]) if i + 1 < len(level) else level[i])
+        level = nxt
+    return level[0]
+
+
+def finish_state(state):
+    """o / l: the attention output of a (merged) state ([CS349E-L11] demo 2)."""
+    m, l, o = state
+    return o / l[..., None]
+
+
+def split_bounds(Nk: int, num_splits: int):
+    """Key ranges of a split-KV partition: split c covers [floor(c Nk / S), floor((c+1) Nk / S)).
+
+    The pages split a key row into contiguous segments ([CS349E-L11] demo 2,
+    flash-decoding); this balanced rule is the partition the library documents.
+    """
+    return [((c * Nk) // num_splits, ((c + 1) * Nk) // num_splits) for c in range(num_splits)]
+
+
+def split_partial_states(q, k, v, scale, num_splits: int):
+    """Per-split (m, l, o) for one head: q [Nq, d], k, v [Nk, d] -> list of states over ``split_bounds``."""
+    s = scores_fp64(q, k, scale)
+    v = np.asarray(v, dtype=np.float64)
+    return [partial_state(s[:, a:b], v[a:b]) for a, b in split_bounds(k.shape[0], num_splits)]
+
+
+# ---------------------------------------------------------------------------
+# Brute force for tiny inputs
+# ---------------------------------------------------------------------------
+
+def brute_force_attention(q, k, v, scale):
+    """Literal loops over Python floats with math.exp and math.fsum; for tiny single-head inputs only.
+
+    The standard-attention definition of [FA-Simplified §1.1] evaluated element
+    by element: s_ij = scale sum_c q_ic k_jc; p_ij = exp(s_ij - max_j s_ij);
+    O_i = sum_j p_ij v_j / sum_j p_ij.
+    """
+    q = [[float(x) for x in row] for row in np.asarray(q)]
+    k = [[float(x) for x in row] for row in np.asarray(k)]
+    v = [[float(x) for x in row] for row in np.asarray(v)]
+    out = []
+    for qi in q:
+        s = [float(scale) * math.fsum(a * b for a, b in zip(qi, kj)) for kj in k]
+        mx = max(s)
+        p = [math.exp(x - mx) for x in s]
+        l = math.fsum(p)
+        out.append([math.fsum(p[j] * v[j][c] for j in range(len(k))) / l for c in range(len(v[0]))])
+    return np.array(out)
+
+
+# ---------------------------------------------------------------------------
+# Low-precision rounding of P (the precision demo)
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even) and return them widened to float64.
+
+    [CS349E-L11] demo 4 casts P to BF16 before P.V while m, l and the
+    accumulator stay in FP32. Rounding is done on the float32 bit pattern: add
+    0x7FFF plus the lowest kept bit, then clear the low 16 bits.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return (r.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def round_to_f16(x) -> np.ndarray:
+    """Round float32 values to the nearest IEEE half (ties to even), widened to float64 ([CS349E-L11] demo 4)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
