@@ -1,0 +1,188 @@
+"""Benchmark of the FlashAttention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|long_seq|decode] [--no-cpu]
+
+A step is one fa_fwd over the whole batch (headline, long_seq) or one fa_fwd_split + fa_merge_states
+pair (decode). Inputs are generated and resident in HBM before the timed region. Prints ONE JSON line.
+The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+HBM_PEAK_GBS = 8000.0
+METRIC = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 bf16; % of MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="headline", choices=["headline", "long_seq", "decode"])
+    p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    return p.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "flashattention_forward_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on this exact source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, o_gpu, max_heads):
+    """Time the fp64 oracle on a bounded sample of the same workload (whole heads), on this host's cores."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    from threadpoolctl import threadpool_info
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+    errs = []
+    t0 = time.perf_counter()
+    done = 0
+    for (b, h) in heads:
+        qh, kh, vh = (si.torch_to_f64(x[b, h]) for x in (q, k, v))
+        ref = oracle.attention_fp64(qh[None], kh[None], vh[None], w.scale)[0]
+        got = si.torch_to_f64(o_gpu[b, h])
+        errs.append((float(np.max(np.abs(got - ref))), float(np.linalg.norm(got - ref)), float(np.linalg.norm(ref))))
+        done += 1
+        if time.perf_counter() - t0 > 25.0:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * done * w.Nq * w.Nk * w.d
+    max_abs = max(e[0] for e in errs)
+    rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / (sum(e[2] ** 2 for e in errs) ** 0.5)
+    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+             "sample": f"{done} of {w.B * w.H} heads (all {w.Nq} query rows each) of the same inputs, "
+                       f"{dt:.1f} s wall, fp64 numpy"},
+            {"max_abs": max_abs, "rel_l2": rel, "heads_checked": done})
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not implemented "
+                                   "(heads shard across GPUs with no exchange; see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+    import flashattention_forward_02_amd as fa
+    import seeded_inputs as si
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "decode": si.DECODE_BF16}[args.workload]
+
+    if args.workload == "decode":
+        q, k, v = si.decode_inputs_device(wl, dev)
+    else:
+        qh, kh, vh = si.workload_inputs(wl)
+        q, k, v = qh.to_torch(dev), kh.to_torch(dev), vh.to_torch(dev)
+        del qh, kh, vh
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    if args.workload == "decode":
+        S = wl.num_splits
+        pm = torch.empty((S, wl.B, wl.H, wl.Nq), device=dev, dtype=torch.float32)
+        pl = torch.empty_like(pm)
+        po = torch.empty((S, wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32)
+        o = torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32)
+        order = si.merge_order(wl.seed, S)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fa.fwd_split(q, k, v, S, scale=wl.scale, workspace=(pm, pl, po))
+            if ev is not None:
+                ev[1].record(stream)
+            fa.merge_states(pm, pl, po, order=order, out=o)
+    else:
+        o = torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32)
+
+        def step(ev=None):
+            fa.fwd(q, k, v, scale=wl.scale, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)] \
+        if args.workload == "decode" else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_start.record(stream)
+    for i in range(args.steps):
+        step(kev[i] if kev else None)
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev_start.elapsed_time(ev_end)
+    ms_per_step = gpu_ms / args.steps
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic (seeded N(0,1) draws, see seeded_inputs)"}
+    if args.workload == "decode":
+        split_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+        kv_bytes = 2.0 * wl.B * wl.H * wl.Nk * wl.d * 2
+        alg_bytes = kv_bytes + wl.B * wl.H * wl.d * 2 + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4
+        step_bytes = alg_bytes + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4 + wl.B * wl.H * wl.d * 4
+        result.update({"metric": "split-KV decode HBM GB/s (K+V bytes / step time)", "unit": "GB/s",
+                       "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "Nk": wl.Nk, "d": wl.d,
+                                  "num_splits": wl.num_splits, "merge_order": "default_rng(5).permutation(16)"}})
+        achieved = alg_bytes / (split_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "kernel": "decode_kernel (split)", "achieved": achieved,
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                              "avg_launch_ms": split_ms,
+                              "traffic": traffic_for("decode", source_hash("decode.hip"))}
+        result["step_bytes"] = step_bytes
+    else:
+        flops = wl.flops
+        tflops = flops / (ms_per_step * 1e-3) / 1e12
+        result.update({"unit": "TFLOP/s", "value": tflops,
+                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
+                                  "causal": False, "out_dtype": "fp32"}})
+        result["roofline"] = {"bound": "mfma", "kernel": "fwd_mfma_kernel", "achieved": tflops,
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "avg_launch_ms": ms_per_step,
+                              "traffic": traffic_for(args.workload, source_hash("fwd_mfma.hip"))}
+    result["wall_s_timed"] = wall
+
+    if not args.no_cpu and args.workload == "headline":
+        base, check = cpu_baseline(wl, q, k, v, o, max_heads=8)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = check
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,127 @@
+"""FlashAttention forward for AMD MI355X (gfx950): Python face of libfa.so.
+
+Every function here marshals torch tensors (device memory, the current HIP stream) into a
+call of the C ABI declared in include/fa.h; all arithmetic runs in the library's HIP kernels.
+Outputs are allocated with torch on the inputs' device (the library itself never allocates).
+
+    O = fwd(q, k, v)                                  # q [B,H,Nq,d], k/v [B,H,Nk,d]
+    part = fwd_split(q, k, v, num_splits=16)          # (m, l, o) partial states per key range
+    O = merge_states(*part, order=[...])              # fold them in the given order
+"""
+from __future__ import annotations
+
+import math
+
+from . import _native
+from ._native import FaError, FA_F32, FA_BF16, FA_F16  # noqa: F401
+
+__all__ = ["fwd", "fwd_split", "merge_states", "FaError", "lib_path"]
+
+lib_path = _native.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return FA_F32
+    if dt == torch.bfloat16:
+        return FA_BF16
+    if dt == torch.float16:
+        return FA_F16
+    raise TypeError(f"unsupported dtype {dt} (float32, bfloat16, float16)")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+
+
+def fwd(q, k, v, scale=None, out_dtype=None, return_stats=False, out=None):
+    """O = softmax(scale * q k^T) v per (b, h); scale defaults to 1/sqrt(d). See fa_fwd in include/fa.h.
+
+    With ``return_stats`` also returns m (row max of the scaled scores) and l (sum of exp(s - m)), fp32 [B,H,Nq].
+    """
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, H, Nq, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of out_dtype")
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _native.check(_native.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 m.data_ptr() if m is not None else None, l.data_ptr() if l is not None else None,
+                                 B, H, Nq, Nk, d, float(scale), _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                 _stream_ptr(q.device)))
+    return (out, m, l) if return_stats else out
+
+
+def fwd_split(q, k, v, num_splits, scale=None, workspace=None):
+    """Split-KV partial states (part_m [S,B,H,Nq], part_l, part_o [S,B,H,Nq,d], fp32). See fa_fwd_split."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        part_m = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+        part_l = torch.empty_like(part_m)
+        part_o = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    else:
+        part_m, part_l, part_o = workspace
+    _native.check(_native.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), part_m.data_ptr(),
+                                       part_l.data_ptr(), part_o.data_ptr(), num_splits, B, H, Nq, Nk, d,
+                                       float(scale), _dtype_code(q.dtype), _stream_ptr(q.device)))
+    return part_m, part_l, part_o
+
+
+def merge_states(part_m, part_l, part_o, order=None, out_dtype=None, return_stats=False, out=None):
+    """Fold partial states in ``order`` (default 0..S-1) into O [B,H,Nq,d]. See fa_merge_states."""
+    torch = _torch()
+    S, B, H, Nq, d = part_o.shape
+    for t in (part_m, part_l, part_o):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partial states must be contiguous float32")
+    if part_m.shape != (S, B, H, Nq) or part_l.shape != (S, B, H, Nq):
+        raise ValueError("part_m / part_l must be [S, B, H, Nq]")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=part_o.device)
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, Nq), dtype=torch.float32, device=part_o.device)
+        l = torch.empty((B, H, Nq), dtype=torch.float32, device=part_o.device)
+    _native.check(_native.fa_merge_states(part_m.data_ptr(), part_l.data_ptr(), part_o.data_ptr(),
+                                          None if order is None else list(order), S, B, H, Nq, d, out.data_ptr(),
+                                          _dtype_code(out_dtype), m.data_ptr() if m is not None else None,
+                                          l.data_ptr() if l is not None else None, _stream_ptr(part_o.device)))
+    return (out, m, l) if return_stats else out

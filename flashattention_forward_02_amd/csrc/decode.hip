@@ -1,0 +1,251 @@
+// Split-KV / few-query forward: one workgroup per (key range, query row, head).
+//
+// The flash-decoding decomposition of "CS349E 第 11 讲 01_online_softmax.py" (demo 2
+// observations): different compute units take different key segments of the same query and
+// each produces the partial state (m, l, o) of its segment, o unnormalised. With one query
+// row there is nothing to share between rows, so this path streams K and V once with
+// coalesced 16-byte loads and does the arithmetic on the VALU; it is bound by HBM bandwidth.
+//
+// Inside a workgroup the 256 lanes form 16 groups of 16; a group takes U keys at a time
+// (group g owns keys kbeg + g*U + 16*U*i + u), lane t of the group owns columns
+// [t*D/16, (t+1)*D/16) of q, of the K and V rows and of its accumulator. A score is D/16
+// FMAs per lane plus a butterfly over the group; each group runs the online-softmax
+// recurrence of "FlashAttention 简化版：Tiling + Online Softmax" §2.3 over its keys, and the 16
+// group states are merged at the end with the merge rule of the decoding demo.
+//
+// fp32 inputs use s = scale * (q . k) and the accurate expf (the fp32 accuracy path);
+// bf16/fp16 inputs use base-2 scores, exp(s - m) = 2^(raw*c - m*c) with c = scale*log2(e).
+
+#include <type_traits>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGroups = kThreads / 16;
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+// Load N consecutive elements of T and widen them to fp32.
+template <typename T, int N>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[N]) {
+  if constexpr (std::is_same<T, float>::value) {
+    static_assert(N % 4 == 0, "");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p + i);
+      out[i] = __uint_as_float(x[0]);
+      out[i + 1] = __uint_as_float(x[1]);
+      out[i + 2] = __uint_as_float(x[2]);
+      out[i + 3] = __uint_as_float(x[3]);
+    }
+  } else {
+    static_assert(N == 4 || N == 8, "");
+    unsigned w[N / 2];
+    if constexpr (N == 8) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+      w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+    } else {
+      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+      w[0] = x[0]; w[1] = x[1];
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      if constexpr (std::is_same<T, __bf16>::value) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      } else {
+        out[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xffffu));
+        out[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
+      }
+    }
+  }
+}
+
+// sum += x with the rounding error carried in comp (Kahan); used on the fp32 path, where many keys
+// share the weight and plain fp32 accumulation would lose ~sqrt(Nk) ulps of the nearly
+// cancelling sum p v.
+__device__ __forceinline__ void kahan_add(float& sum, float& comp, float x) {
+  const float y = x - comp;
+  const float t = sum + y;
+  comp = (t - sum) - y;
+  sum = t;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* base, size_t elem, int out_dtype, float x) {
+  if (out_dtype == kF32) static_cast<float*>(base)[elem] = x;
+  else if (out_dtype == kBF16) static_cast<__bf16*>(base)[elem] = (__bf16)x;
+  else static_cast<_Float16*>(base)[elem] = (_Float16)x;
+}
+
+template <int D, typename T, int U>
+__global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
+  constexpr bool kAccurate = std::is_same<T, float>::value;
+  constexpr int DL = D / 16;  // columns per lane
+  __shared__ float sh_m[kGroups], sh_l[kGroups];
+  __shared__ float sh_o[kGroups][D];
+
+  const int S = a.num_splits;
+  const int split = blockIdx.x % S;
+  const int rest = blockIdx.x / S;
+  const int row = rest % a.Nq;
+  const size_t head = rest / a.Nq;
+  const int kbeg = split_begin(split, a.Nk, S);
+  const int kend = split_begin(split + 1, a.Nk, S);
+
+  const int tid = threadIdx.x;
+  const int g = tid >> 4;
+  const int t = tid & 15;
+  const T* __restrict__ Qr = static_cast<const T*>(a.q) + (head * a.Nq + row) * (size_t)D + t * DL;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + head * (size_t)a.Nk * D + t * DL;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + head * (size_t)a.Nk * D + t * DL;
+
+  float q[DL];
+  load_row<T, DL>(Qr, q);
+  const float c2 = a.scale_log2e;
+
+  float m = -INFINITY, l = 0.f, lcomp = 0.f, acc[DL], comp[DL];
+#pragma unroll
+  for (int c = 0; c < DL; ++c) acc[c] = comp[c] = 0.f;
+
+  for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
+    float kx[U][DL], vx[U][DL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u;
+      if (key < kend) {
+        load_row<T, DL>(K + (size_t)key * D, kx[u]);
+        load_row<T, DL>(V + (size_t)key * D, vx[u]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;
+      }
+    }
+    float s[U];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) dot = __builtin_fmaf(q[c], kx[u][c], dot);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) dot += __shfl_xor(dot, off);
+      const bool ok = base + u < kend;
+      s[u] = ok ? (kAccurate ? a.scale * dot : dot) : -INFINITY;
+      mx = fmaxf(mx, s[u]);
+    }
+    const float mnew = fmaxf(m, mx);
+    float alpha;
+    if constexpr (kAccurate) alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
+    else alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c2);
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) acc[c] *= alpha;
+    if constexpr (kAccurate) {
+      lcomp *= alpha;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) comp[c] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float p;
+      if constexpr (kAccurate) p = expf(s[u] - mnew);
+      else p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u], c2, -mnew * c2));
+      if (s[u] == -INFINITY) p = 0.f;
+      if constexpr (kAccurate) {
+        kahan_add(l, lcomp, p);
+#pragma unroll
+        for (int c = 0; c < DL; ++c) {
+          const float y = __builtin_fmaf(p, vx[u][c], -comp[c]);
+          const float t2 = acc[c] + y;
+          comp[c] = (t2 - acc[c]) - y;
+          acc[c] = t2;
+        }
+      } else {
+        l += p;
+#pragma unroll
+        for (int c = 0; c < DL; ++c) acc[c] = __builtin_fmaf(p, vx[u][c], acc[c]);
+      }
+    }
+    m = mnew;
+  }
+
+  // ---- merge the 16 group states ----
+  if (t == 0) {
+    sh_m[g] = m;
+    sh_l[g] = l;
+  }
+#pragma unroll
+  for (int c = 0; c < DL; ++c) sh_o[g][t * DL + c] = acc[c];
+  __syncthreads();
+
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) M = fmaxf(M, sh_m[i]);
+  float w[kGroups];
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) {
+    const float mi = sh_m[i];
+    if (mi == -INFINITY) w[i] = 0.f;
+    else if constexpr (kAccurate) w[i] = expf(mi - M);
+    else w[i] = __builtin_amdgcn_exp2f((mi - M) * c2);
+    L = __builtin_fmaf(w[i], sh_l[i], L);
+  }
+  const float m_nat = kAccurate ? M : a.scale * M;
+  const size_t qrow = head * a.Nq + row;
+  for (int c = tid; c < D; c += kThreads) {
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) o = __builtin_fmaf(w[i], sh_o[i][c], o);
+    if (a.split_mode == 0) {
+      store_out<T>(a.o, qrow * D + c, a.out_dtype, o / L);
+    } else {
+      const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
+      a.part_o[prow * D + c] = o;
+    }
+  }
+  if (tid == 0) {
+    if (a.split_mode == 0) {
+      if (a.m_out) a.m_out[qrow] = m_nat;
+      if (a.l_out) a.l_out[qrow] = L;
+    } else {
+      const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
+      a.part_m[prow] = m_nat;
+      a.part_l[prow] = L;
+    }
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
+  constexpr int U = (D == 64) ? 8 : 4;
+  const long long nwg = (long long)a.num_splits * a.Nq * a.H * a.B;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  FwdArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U>), dim3((unsigned)nwg),
+                         dim3(kThreads), kargs, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s) {
+  if (in_dtype == kF32) {
+    if (d == 64) return launch_typed<64, float>(a, s);
+    if (d == 128) return launch_typed<128, float>(a, s);
+  } else if (in_dtype == kBF16) {
+    if (d == 64) return launch_typed<64, __bf16>(a, s);
+    if (d == 128) return launch_typed<128, __bf16>(a, s);
+  } else if (in_dtype == kF16) {
+    if (d == 64) return launch_typed<64, _Float16>(a, s);
+    if (d == 128) return launch_typed<128, _Float16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,191 @@
+// C ABI of libfa.so: argument validation, kernel selection and error reporting.
+// The contract of every entry point is documented in include/fa.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool valid_dtype(int dt) { return dt == FA_F32 || dt == FA_BF16 || dt == FA_F16; }
+size_t dtype_size(int dt) { return dt == FA_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// Shape, dtype and scale checks shared by fa_fwd and fa_fwd_split.
+fa_status check_common(const char* fn, const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk,
+                       int d, float scale, int in_dtype) {
+  if (B < 0 || H < 0 || Nq < 0) return fail(FA_EINVAL, "%s: B=%d, H=%d, Nq=%d must be >= 0", fn, B, H, Nq);
+  if (Nk < 1) return fail(FA_EINVAL, "%s: Nk=%d; softmax over an empty key set is undefined (Nk >= 1)", fn, Nk);
+  // A pointer may be NULL only when its tensor holds no elements.
+  const bool no_q = (size_t)B * H * Nq == 0, no_kv = (size_t)B * H == 0;
+  if ((!q && !no_q) || ((!k || !v) && !no_kv))
+    return fail(FA_EINVAL, "%s: q, k and v must be non-NULL device pointers", fn);
+  if (!valid_dtype(in_dtype)) return fail(FA_EINVAL, "%s: in_dtype=%d is not FA_F32, FA_BF16 or FA_F16", fn, in_dtype);
+  if (!(scale >= 0.f) || !isfinite(scale)) return fail(FA_EINVAL, "%s: scale=%g must be finite and >= 0", fn, (double)scale);
+  if (d <= 0) return fail(FA_EINVAL, "%s: d=%d must be > 0", fn, d);
+  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "%s: head dimension d=%d (supported: 64, 128)", fn, d);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FA_EINVAL, "%s: q, k and v must be 16-byte aligned", fn);
+  return FA_OK;
+}
+
+fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, float scale) {
+  fa::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.num_splits = 1;
+  a.scale = scale;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  return a;
+}
+
+fa_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(FA_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
+                 int Nq, int Nk, int d, float scale, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  fa_status st = check_common("fa_fwd", q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+  if (st != FA_OK) return st;
+  if (!o && (size_t)B * H * Nq != 0) return fail(FA_EINVAL, "fa_fwd: o must be a non-NULL device pointer");
+  if (out_dtype != FA_F32 && out_dtype != in_dtype)
+    return fail(FA_EINVAL, "fa_fwd: out_dtype=%d must be FA_F32 or equal to in_dtype=%d", (int)out_dtype, (int)in_dtype);
+  if (!aligned16(o)) return fail(FA_EINVAL, "fa_fwd: o must be 16-byte aligned");
+  if (!aligned4(m_out) || !aligned4(l_out)) return fail(FA_EINVAL, "fa_fwd: m_out and l_out must be 4-byte aligned");
+  if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
+  const size_t heads = (size_t)B * H;
+  const size_t obytes = heads * Nq * d * dtype_size(out_dtype);
+  const size_t qbytes = heads * Nq * d * dtype_size(in_dtype), kvbytes = heads * Nk * d * dtype_size(in_dtype);
+  if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, kvbytes) || overlaps(o, obytes, v, kvbytes))
+    return fail(FA_EINVAL, "fa_fwd: o overlaps q, k or v");
+
+  fa::FwdArgs a = make_args(q, k, v, B, H, Nq, Nk, scale);
+  a.o = o;
+  a.m_out = m_out;
+  a.l_out = l_out;
+  a.out_dtype = out_dtype;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
+  else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
+  else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
+  return launched("fa_fwd", e);
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,
+                       int num_splits, int B, int H, int Nq, int Nk, int d, float scale, fa_dtype in_dtype,
+                       void* stream) {
+  g_last_error[0] = 0;
+  fa_status st = check_common("fa_fwd_split", q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+  if (st != FA_OK) return st;
+  if ((!part_m || !part_l || !part_o) && (size_t)B * H * Nq != 0)
+    return fail(FA_EINVAL, "fa_fwd_split: part_m, part_l and part_o must be non-NULL");
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS || num_splits > Nk)
+    return fail(FA_EINVAL, "fa_fwd_split: num_splits=%d must be in [1, min(Nk=%d, %d)]", num_splits, Nk, FA_MAX_SPLITS);
+  if (!aligned16(part_o) || !aligned4(part_m) || !aligned4(part_l))
+    return fail(FA_EINVAL, "fa_fwd_split: part_o must be 16-byte and part_m, part_l 4-byte aligned");
+  if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
+
+  fa::FwdArgs a = make_args(q, k, v, B, H, Nq, Nk, scale);
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_o = part_o;
+  a.num_splits = num_splits;
+  a.split_mode = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
+  else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
+  else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
+  return launched("fa_fwd_split", e);
+}
+
+fa_status fa_merge_states(const float* part_m, const float* part_l, const float* part_o, const int* order,
+                          int num_splits, int B, int H, int Nq, int d, void* o, fa_dtype out_dtype, float* m_out,
+                          float* l_out, void* stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || H < 0 || Nq < 0) return fail(FA_EINVAL, "fa_merge_states: B=%d, H=%d, Nq=%d must be >= 0", B, H, Nq);
+  if ((!part_m || !part_l || !part_o || !o) && (size_t)B * H * Nq != 0)
+    return fail(FA_EINVAL, "fa_merge_states: part_m, part_l, part_o and o must be non-NULL");
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS)
+    return fail(FA_EINVAL, "fa_merge_states: num_splits=%d must be in [1, %d]", num_splits, FA_MAX_SPLITS);
+  if (!valid_dtype(out_dtype)) return fail(FA_EINVAL, "fa_merge_states: out_dtype=%d is not a fa_dtype", (int)out_dtype);
+  if (d <= 0) return fail(FA_EINVAL, "fa_merge_states: d=%d must be > 0", d);
+  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "fa_merge_states: head dimension d=%d (supported: 64, 128)", d);
+  if (!aligned16(part_o) || !aligned16(o) || !aligned4(part_m) || !aligned4(part_l) || !aligned4(m_out) ||
+      !aligned4(l_out))
+    return fail(FA_EINVAL, "fa_merge_states: part_o and o must be 16-byte aligned, the rest 4-byte aligned");
+
+  fa::MergeArgs a;
+  memset(&a, 0, sizeof(a));
+  bool seen[FA_MAX_SPLITS] = {false};
+  for (int i = 0; i < num_splits; ++i) {
+    const int s = order ? order[i] : i;
+    if (s < 0 || s >= num_splits || seen[s])
+      return fail(FA_EINVAL, "fa_merge_states: order is not a permutation of 0..%d (entry %d = %d)", num_splits - 1, i, s);
+    seen[s] = true;
+    a.order[i] = (unsigned short)s;
+  }
+  const long long rows = (long long)B * H * Nq;
+  if (rows == 0) return FA_OK;
+  if (rows > 0x7fffffffLL) return fail(FA_EINVAL, "fa_merge_states: B*H*Nq=%lld exceeds 2^31-1", rows);
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_o = part_o;
+  a.o = o;
+  a.m_out = m_out;
+  a.l_out = l_out;
+  a.S = num_splits;
+  a.rows = (int)rows;
+  a.out_dtype = out_dtype;
+  return launched("fa_merge_states", fa::launch_merge(a, d, static_cast<hipStream_t>(stream)));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_EINVAL: return "FA_EINVAL";
+    case FA_EUNSUPPORTED: return "FA_EUNSUPPORTED";
+    case FA_EHIP: return "FA_EHIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

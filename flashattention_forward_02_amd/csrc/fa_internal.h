@@ -1,0 +1,68 @@
+// Internal declarations shared by the host API (fa_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Arguments of one forward launch. In full mode (split_mode == 0) the kernels write the
+// normalised O (out_dtype) and, when non-null, m_out / l_out. In split mode they write the
+// unnormalised partial states part_m / part_l / part_o of each key range.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* m_out;
+  float* l_out;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  int B, H, Nq, Nk;
+  int num_splits;   // 1 in full mode
+  int split_mode;   // 0: final output, 1: partial states
+  int out_dtype;    // Dtype of o (full mode)
+  float scale;      // softmax scale applied to q.k (natural-log units)
+  float scale_log2e;  // scale * log2(e): scores in base-2 units for exp2
+};
+
+// Merge arguments. The merge order travels inside the kernel arguments.
+constexpr int kMaxSplits = 256;
+struct MergeArgs {
+  const float* part_m;
+  const float* part_l;
+  const float* part_o;
+  void* o;
+  float* m_out;
+  float* l_out;
+  int S, rows;      // rows = B * H * Nq
+  int out_dtype;
+  unsigned short order[kMaxSplits];
+};
+
+// Key range [split_begin(c), split_begin(c + 1)) of part c of a split-KV partition.
+__host__ __device__ inline int split_begin(int c, int Nk, int S) {
+  return (int)(((long long)c * (long long)Nk) / (long long)S);
+}
+
+// Workgroup remap so that consecutive logical tiles run on one XCD. The dispatcher hands
+// workgroup i of a 1-D grid to XCD i % 8; tiles of one head share K/V, and keeping them on
+// one XCD keeps that K/V in one L2.
+__device__ inline int xcd_remap(int wg, int nwg) {
+  if ((nwg & 7) != 0) return wg;
+  return (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+hipError_t launch_fwd_mfma(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t s);
+
+// Query-row count up to which the split/decode kernel (one workgroup per query row and key
+// range) is used instead of the tiled kernels.
+constexpr int kDecodeMaxNq = 16;
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of libfa.so, a FlashAttention forward pass for AMD MI355X (gfx950).
+ *
+ * The operation (one attention head; every (b, h) pair is independent):
+ *
+ *     S = scale * Q K^T                        [Nq, Nk]
+ *     P = softmax(S) along each row            [Nq, Nk]
+ *     O = P V                                  [Nq, d]
+ *
+ * as defined by "FlashAttention 简化版：Tiling + Online Softmax" (forceinjection.github.io), §1.1,
+ * and computed the way §2.3 and §3.1 of that page lay out: Q is cut into row tiles, K and V
+ * stream past each Q tile in key tiles, and every query row keeps a running maximum m, a
+ * running sum l of exp(s - m) and an accumulator; when a key tile raises m, l and the
+ * accumulator are scaled by exp(m_old - m_new), and the accumulator is divided by l once,
+ * after the last key tile. No [Nq, Nk] matrix is ever written to memory.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense and contiguous, row-major with d innermost: Q [B, H, Nq, d],
+ *     K and V [B, H, Nk, d], O [B, H, Nq, d]. Element (b, h, i, c) sits at
+ *     ((b*H + h)*N + i)*d + c. d (the head dimension) must be 64 or 128.
+ *   - Every pointer is a device pointer (hipMalloc / torch memory) aligned to 16 bytes
+ *     (m_out, l_out, part_m, part_l: 4 bytes). A pointer may be NULL only when its tensor
+ *     holds no elements. The caller owns all memory. The library never allocates device memory.
+ *   - Arithmetic: scores, the running maximum m, the running sum l and the output
+ *     accumulator are fp32 for every input type. With bf16/fp16 inputs the two products
+ *     QK^T and PV run on the matrix cores with fp32 accumulation; the probabilities P are
+ *     rounded to the input type (round to nearest even) for PV only, while l sums the
+ *     unrounded fp32 values -- the precision scheme of demo 4 of "CS349E 第 11 讲
+ *     01_online_softmax.py".
+ *   - m_out / l_out (optional, NULL to skip), shape [B, H, Nq] fp32: m is the row maximum of
+ *     S and l = sum_j exp(S_ij - m), so softmax(S)_ij = exp(S_ij - m_i) / l_i (the statistics
+ *     Exercise 5 of "Flash Attention 代码填空 (Level 2-3)" keeps for the backward pass).
+ *   - All calls are asynchronous on `stream` (a hipStream_t; NULL means the null stream).
+ *   - Errors: every call validates its arguments on the host before touching the device and
+ *     returns a status; nothing aborts, throws or prints. FA_EINVAL: a bad pointer, size,
+ *     dtype, scale or alignment. FA_EUNSUPPORTED: a valid request this build does not
+ *     implement (e.g. d = 96). FA_EHIP: the HIP runtime reported an error when launching.
+ *     fa_last_error() then returns a description (per thread, valid until the next call).
+ *     B*H = 0 or Nq = 0 is a successful no-op. Nk must be >= 1 (softmax over no keys is
+ *     undefined). Calls that overlap on one stream are ordered; calls on different streams
+ *     that write the same buffers race.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+#define FA_MAX_SPLITS 256
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
+
+typedef enum { FA_OK = 0, FA_EINVAL = 1, FA_EUNSUPPORTED = 2, FA_EHIP = 3 } fa_status;
+
+/*
+ * fa_fwd -- O = softmax(scale * Q K^T) V for every (b, h).
+ *
+ * Defined by "FlashAttention 简化版：Tiling + Online Softmax" §1.1 (standard attention) and
+ * computed as its §3.1 tiled loop with the online-softmax state of §2.3.
+ *   q, k, v   [B,H,Nq,d], [B,H,Nk,d], [B,H,Nk,d] in `in_dtype` (FA_F32, FA_BF16, FA_F16).
+ *   o         [B,H,Nq,d] in `out_dtype`, which is FA_F32 or equal to `in_dtype`.
+ *   m_out, l_out  optional [B,H,Nq] fp32 row statistics (see above), or NULL.
+ *   scale     finite and >= 0; usually 1/sqrt(d) (the pages' scale). 0 gives uniform weights.
+ * o must not overlap q, k or v.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
+                 float* m_out, float* l_out,
+                 int B, int H, int Nq, int Nk, int d, float scale,
+                 fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_split -- split-KV partial states (flash-decoding).
+ *
+ * The key range of every head is cut into `num_splits` contiguous parts; part c covers keys
+ * [floor(c*Nk/num_splits), floor((c+1)*Nk/num_splits)) and is never empty. For each part the
+ * call writes the partial state (m, l, o) of "CS349E 第 11 讲 01_online_softmax.py" demo 2:
+ *   part_m [S,B,H,Nq] fp32   m = max over the part's keys of S_ij
+ *   part_l [S,B,H,Nq] fp32   l = sum over the part's keys of exp(S_ij - m)
+ *   part_o [S,B,H,Nq,d] fp32 o = sum over the part's keys of exp(S_ij - m) * V_j  (NOT divided by l)
+ * with S = num_splits, 1 <= num_splits <= min(Nk, FA_MAX_SPLITS). fa_merge_states combines
+ * them; the merged result equals fa_fwd's up to rounding. The caller owns the three buffers.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v,
+                       float* part_m, float* part_l, float* part_o,
+                       int num_splits, int B, int H, int Nq, int Nk, int d, float scale,
+                       fa_dtype in_dtype, void* stream);
+
+/*
+ * fa_merge_states -- fold partial states into the attention output.
+ *
+ * For every (b, h, i) the states of the `num_splits` parts are merged one after another in
+ * the order given by `order` (a host array holding a permutation of 0..num_splits-1, read
+ * during the call; NULL means 0, 1, ..., num_splits-1). One merge step is
+ *   m = max(m_a, m_b); l = l_a e^(m_a - m) + l_b e^(m_b - m); o = o_a e^(m_a - m) + o_b e^(m_b - m),
+ * the rule that makes the result independent of the order up to rounding ("CS349E 第 11 讲
+ * 01_online_softmax.py" demo 2, derived from the recurrence of "从零手写 FlashAttention" §4).
+ * A part with m = -inf (no keys) has weight 0. Finally O = o / l in `out_dtype` (FA_F32,
+ * FA_BF16 or FA_F16), and, when not NULL, m_out / l_out receive the merged m and l.
+ * Layouts as in fa_fwd_split; o is [B,H,Nq,d].
+ */
+fa_status fa_merge_states(const float* part_m, const float* part_l, const float* part_o,
+                          const int* order, int num_splits, int B, int H, int Nq, int d,
+                          void* o, fa_dtype out_dtype, float* m_out, float* l_out, void* stream);
+
+/* Name of a status code ("FA_OK", ...); never NULL. */
+const char* fa_status_string(int status);
+
+/* Description of the last non-OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and rejects bad
+arguments with the documented status before touching the device (CPU only; no compute calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import flashattention_forward_02_amd as fa
+from flashattention_forward_02_amd import _native as n
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, 16-byte aligned, never dereferenced: every call below fails validation first.
+P = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(n.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", n.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for f in declared_functions():
+        assert f in syms, f
+        assert hasattr(n.lib(), f)
+
+
+def test_abi_version_and_status_strings():
+    assert n.fa_abi_version() == 1
+    assert [n.fa_status_string(s) for s in range(4)] == ["FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
+    assert n.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P * 2, m_out=None, l_out=None, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125,
+             in_dtype=n.FA_BF16, out_dtype=n.FA_F32, stream=None)
+    a.update(kw)
+    return n.fa_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), n.FA_EINVAL, "non-NULL"),
+    (dict(o=None), n.FA_EINVAL, "non-NULL"),
+    (dict(Nk=0), n.FA_EINVAL, "empty key set"),
+    (dict(B=-1), n.FA_EINVAL, ">= 0"),
+    (dict(Nq=-3), n.FA_EINVAL, ">= 0"),
+    (dict(in_dtype=7), n.FA_EINVAL, "in_dtype"),
+    (dict(out_dtype=n.FA_F16), n.FA_EINVAL, "out_dtype"),
+    (dict(scale=-1.0), n.FA_EINVAL, "scale"),
+    (dict(scale=float("nan")), n.FA_EINVAL, "scale"),
+    (dict(scale=float("inf")), n.FA_EINVAL, "scale"),
+    (dict(d=96), n.FA_EUNSUPPORTED, "d=96"),
+    (dict(d=0), n.FA_EINVAL, "d=0"),
+    (dict(q=P + 2), n.FA_EINVAL, "aligned"),
+    (dict(o=P * 2 + 8), n.FA_EINVAL, "aligned"),
+    (dict(m_out=P + 2), n.FA_EINVAL, "aligned"),
+    (dict(o=P), n.FA_EINVAL, "overlaps"),
+])
+def test_fa_fwd_rejects(kw, status, msg):
+    assert fwd(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_fa_fwd_empty_work_is_ok_without_device():
+    assert fwd(Nq=0) == n.FA_OK
+    assert fwd(B=0) == n.FA_OK
+    assert n.fa_last_error() == ""
+    # empty tensors may come with NULL pointers (torch hands out NULL for zero elements)
+    assert fwd(Nq=0, q=None, o=None) == n.FA_OK
+    assert fwd(B=0, q=None, k=None, v=None, o=None) == n.FA_OK
+    assert fwd(Nq=0, k=None) == n.FA_EINVAL      # K still holds B*H*Nk elements
+
+
+def split(**kw):
+    a = dict(q=P, k=P, v=P, part_m=P * 2, part_l=P * 3, part_o=P * 4, num_splits=4, B=1, H=1, Nq=1, Nk=64, d=128,
+             scale=0.1, in_dtype=n.FA_BF16, stream=None)
+    a.update(kw)
+    return n.fa_fwd_split(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(part_o=None), n.FA_EINVAL), (dict(num_splits=0), n.FA_EINVAL), (dict(num_splits=65), n.FA_EINVAL),
+    (dict(num_splits=300, Nk=1000), n.FA_EINVAL), (dict(d=32), n.FA_EUNSUPPORTED), (dict(Nk=0), n.FA_EINVAL),
+    (dict(part_o=P * 4 + 4), n.FA_EINVAL),
+])
+def test_fa_fwd_split_rejects(kw, status):
+    assert split(**kw) == status
+    assert n.fa_last_error() != ""
+
+
+def merge(**kw):
+    a = dict(part_m=P, part_l=P * 2, part_o=P * 3, order=None, num_splits=4, B=1, H=1, Nq=1, d=64, o=P * 4,
+             out_dtype=n.FA_F32, m_out=None, l_out=None, stream=None)
+    a.update(kw)
+    return n.fa_merge_states(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(order=[0, 1, 1, 2]), n.FA_EINVAL, "permutation"),
+    (dict(order=[0, 1, 2, 4]), n.FA_EINVAL, "permutation"),
+    (dict(order=[-1, 1, 2, 3]), n.FA_EINVAL, "permutation"),
+    (dict(num_splits=0, order=None), n.FA_EINVAL, "num_splits"),
+    (dict(num_splits=257), n.FA_EINVAL, "num_splits"),
+    (dict(out_dtype=5), n.FA_EINVAL, "out_dtype"),
+    (dict(d=256), n.FA_EUNSUPPORTED, "d=256"),
+    (dict(o=None), n.FA_EINVAL, "non-NULL"),
+])
+def test_fa_merge_states_rejects(kw, status, msg):
+    assert merge(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_merge_empty_rows_ok():
+    assert merge(order=[3, 1, 0, 2], Nq=0) == n.FA_OK
+
+
+def test_binding_raises_typed_errors():
+    with pytest.raises(n.FaError) as e:
+        n.check(fwd(Nk=0))
+    assert e.value.status == n.FA_EINVAL and "FA_EINVAL" in str(e.value)
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The library package imports nothing from the oracle and carries no CPU implementation of the op."""
+    pkg = os.path.dirname(fa.__file__)
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(from|import)\s+(oracle|seeded_inputs)", src, flags=re.M), name
+            for op in (".softmax(", "einsum(", "matmul(", "scaled_dot_product_attention", ".exp(", " @ "):
+                assert op not in src, (name, op)

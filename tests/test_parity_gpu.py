@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Tolerances live in tests/_parity.py. Small cases span several tiles and ragged tails; the
+workload-size cases compare sampled rows that the oracle computes one head at a time.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from tests._parity import assert_close, assert_stats, errors, stat_bound
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import flashattention_forward_02_amd as fa
+    from flashattention_forward_02_amd import _native as n
+
+DEV = "cuda:0"
+TORCH_DT = {"f32": None, "bf16": None, "f16": None}
+
+
+def _tdt(dtype):
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(q, k, v, dtype, scale, out_dtype="f32", stats=True):
+    """Run fa_fwd on host Tensors; return O, m, l as float64 numpy plus the device tensors."""
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    o, m, l = fa.fwd(qd, kd, vd, scale=scale, out_dtype=_tdt(out_dtype), return_stats=True)
+    torch.cuda.synchronize()
+    return si.torch_to_f64(o), si.torch_to_f64(m), si.torch_to_f64(l)
+
+
+# ---------------------------------------------------------------------------------------------
+# small shapes: several tiles, ragged tails, every dtype and head dim
+# ---------------------------------------------------------------------------------------------
+
+SMALL = [
+    # (B, H, Nq, Nk, d)
+    (1, 1, 1, 1, 64),
+    (1, 1, 5, 7, 64),
+    (2, 3, 300, 333, 64),
+    (1, 2, 257, 64, 64),
+    (1, 1, 513, 1000, 128),
+    (2, 1, 64, 129, 128),
+    (1, 1, 17, 4097, 64),
+    (1, 2, 16, 300, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(dtype, shape):
+    B, H, Nq, Nk, d = shape
+    say(f"small case dtype={dtype} shape={shape}")
+    q, k, v = si.small_case(1000 + Nq + Nk, B, H, Nq, Nk, d, dtype)
+    scale = si.fp32_inverse_sqrt(d)
+    o, m, l = run_case(q, k, v, dtype, scale)
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale, return_stats=True)
+    assert_close(o, ref, dtype, f"{dtype} {shape}")
+    assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), scale), f"{dtype} {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_low_precision_output_dtype(dtype):
+    q, k, v = si.small_case(77, 2, 2, 300, 500, 64, dtype)
+    scale = si.fp32_inverse_sqrt(64)
+    o, _, _ = run_case(q, k, v, dtype, scale, out_dtype=dtype)
+    ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale)
+    assert_close(o, ref, dtype, f"{dtype} out")
+
+
+# ---------------------------------------------------------------------------------------------
+# degenerate cases the method has
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_scale_gives_column_mean(dtype):
+    q, k, v = si.small_case(5, 1, 2, 300, 130, 64, dtype)
+    o, m, l = run_case(q, k, v, dtype, 0.0)
+    ref = np.broadcast_to(v.as_f64().mean(axis=2, keepdims=True), o.shape)
+    assert_close(o, ref, dtype, "scale=0")
+    assert np.all(m == 0.0) and np.allclose(l, 130.0, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_returns_v(dtype):
+    q, k, v = si.small_case(6, 1, 1, 300, 1, 128, dtype)
+    o, _, l = run_case(q, k, v, dtype, 0.3)
+    assert np.array_equal(o, np.broadcast_to(v.as_f64(), o.shape)) or errors(o, np.broadcast_to(v.as_f64(), o.shape))[0] < 1e-6
+    assert np.allclose(l, 1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_score_shift(dtype):
+    """Scores near 100 (exp would overflow without the running max) stay finite and correct.
+
+    An fp32 score of magnitude |s| is itself only known to |s| * 2^-24 before the max is
+    subtracted, so at |s| ~ 100 the fp32 bar is scaled by the score size: max_abs and rel_l2
+    within 2^-20 * max|s| (16 half-ulps of the largest score). bf16 keeps its usual bar.
+    """
+    q, k, v = si.small_case(8, 1, 1, 260, 300, 64, dtype)
+    qf = q.as_f64()
+    u = qf[0, 0].mean(axis=0)
+    u = u * (100.0 / (0.125 * float(u @ u)))
+    k2 = si.encode((k.as_f64() + u).astype(np.float32), dtype)
+    o, _, _ = run_case(q, k2, v, dtype, 0.125)
+    ref, m_ref, _ = oracle.attention_fp64(qf, k2.as_f64(), v.as_f64(), 0.125, return_stats=True)
+    assert np.all(np.isfinite(o)) and float(np.max(m_ref)) > 50.0
+    if dtype == "f32":
+        bar = 2.0 ** -20 * float(np.max(np.abs(m_ref)))
+        max_abs, rel_l2 = errors(o, ref)
+        assert max_abs <= bar and rel_l2 <= bar, (max_abs, rel_l2, bar)
+    else:
+        assert_close(o, ref, dtype, "shifted")
+
+
+def test_empty_work_is_noop():
+    q = torch.zeros((1, 2, 0, 64), device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 5, 64), device=DEV, dtype=torch.bfloat16)
+    o = fa.fwd(q, k, k)
+    assert o.shape == (1, 2, 0, 64)
+    q = torch.zeros((0, 2, 4, 64), device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros((0, 2, 5, 64), device=DEV, dtype=torch.bfloat16)
+    assert fa.fwd(q, k, k).shape == (0, 2, 4, 64)
+
+
+def test_device_pointer_validation():
+    x = torch.zeros(4 * 64 + 8, device=DEV, dtype=torch.bfloat16)
+    st = n.fa_fwd(x.data_ptr() + 2, x.data_ptr(), x.data_ptr(), x.data_ptr(), None, None, 1, 1, 4, 4, 64, 0.125,
+                  n.FA_BF16, n.FA_F32, None)
+    assert st == n.FA_EINVAL and "aligned" in n.fa_last_error()
+
+
+def test_raw_c_abi_call_on_current_stream():
+    """Call fa_fwd with raw pointers (no Python wrapper logic) on a side stream."""
+    q, k, v = si.small_case(21, 1, 2, 100, 200, 64, "bf16")
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    o = torch.empty((1, 2, 100, 64), device=DEV, dtype=torch.float32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st = n.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), None, None, 1, 2, 100, 200, 64,
+                      0.125, n.FA_BF16, n.FA_F32, s.cuda_stream)
+    assert st == n.FA_OK, n.fa_last_error()
+    s.synchronize()
+    ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), 0.125)
+    assert_close(si.torch_to_f64(o), ref, "bf16", "raw abi")
+
+
+def test_no_device_allocation_and_no_nxn_buffer():
+    """The library allocates nothing: free device memory is unchanged across a large call, which an
+    N x N fp32 score buffer (4 GiB at B*H=64, N=4096) would not leave unchanged."""
+    w = si.HEADLINE_BF16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1)
+    q = torch.randn((w.B, w.H, w.Nq, w.d), device=DEV, generator=g).to(torch.bfloat16)
+    k = torch.randn((w.B, w.H, w.Nk, w.d), device=DEV, generator=g).to(torch.bfloat16)
+    v = torch.randn((w.B, w.H, w.Nk, w.d), device=DEV, generator=g).to(torch.bfloat16)
+    o = torch.empty((w.B, w.H, w.Nq, w.d), device=DEV, dtype=torch.float32)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    fa.fwd(q, k, v, out=o)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0
+    assert abs(free1 - free0) < 64 * 2 ** 20, (free0, free1)
+
+
+# ---------------------------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------------------------
+
+def test_single_head_fp32_256x64():
+    say("single_head_fp32")
+    q, k, v = si.single_head_fp32()
+    o, m, l = run_case(q, k, v, "f32", 0.125)
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), 0.125, return_stats=True)
+    assert_close(o, ref, "f32", "single head fp32")
+    assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), 0.125))
+
+
+@pytest.mark.parametrize("batched", [False, True])
+def test_one_query_long_keys_fp32(batched):
+    say(f"one_query_long_keys batched={batched}")
+    q, k, v = si.one_query_long_keys(batched=batched)
+    o, m, l = run_case(q, k, v, "f32", 0.125)
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), 0.125, return_stats=True)
+    assert_close(o, ref, "f32", f"one query batched={batched}")
+    assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), 0.125))
+    if batched:
+        q1, k1, v1 = si.one_query_long_keys(batched=False)
+        o1, _, _ = run_case(q1, k1, v1, "f32", 0.125)
+        assert np.max(np.abs(o[0, 0, 0] - o1[0, 0, 0])) < 1e-6
+
+
+def _sampled_rows(w, o, m, l, q, k, v, heads, rows_per_head, seed):
+    r = np.random.default_rng(seed)
+    qf, kf, vf = q.as_f64() if hasattr(q, "as_f64") else q, k, v
+    got, ref, gm, gl, rm, rl, bd = [], [], [], [], [], [], []
+    for (b, h) in heads:
+        rows = np.sort(r.choice(w.Nq, size=min(rows_per_head, w.Nq), replace=False))
+        kh = kf(b, h) if callable(kf) else kf[b, h]
+        vh = vf(b, h) if callable(vf) else vf[b, h]
+        qh = qf(b, h) if callable(qf) else qf[b, h]
+        o_ref, m_ref, l_ref = oracle.attention_rows_fp64(qh[rows], kh, vh, w.scale)
+        got.append(o[b, h, rows]); ref.append(o_ref)
+        gm.append(m[b, h, rows]); gl.append(l[b, h, rows]); rm.append(m_ref); rl.append(l_ref)
+        bd.append(stat_bound(qh[rows], kh, w.scale))
+    return (np.concatenate(got), np.concatenate(ref), np.concatenate(gm), np.concatenate(gl), np.concatenate(rm),
+            np.concatenate(rl), np.concatenate(bd))
+
+
+def test_headline_bf16_full_size():
+    """B=4, H=16, N=4096, d=64 bf16 at full size (the benchmarked launch), sampled rows from 8 heads."""
+    w = si.HEADLINE_BF16
+    say("headline: generating inputs")
+    q, k, v = si.workload_inputs(w)
+    say("headline: running fa_fwd")
+    o, m, l = run_case(q, k, v, "bf16", w.scale)
+    qf, kf, vf = q.as_f64(), k.as_f64(), v.as_f64()
+    heads = [(0, 0), (0, 15), (1, 3), (2, 8), (3, 15), (3, 0), (1, 11), (2, 2)]
+    got, ref, gm, gl, rm, rl, bd = _sampled_rows(w, o, m, l, qf, kf, vf, heads, 256, 3)
+    say(f"headline: errors {errors(got, ref)}")
+    assert_close(got, ref, "bf16", "headline sampled rows")
+    assert_stats(gm, gl, rm, rl, bd, "headline")
+    assert np.all(np.isfinite(o))
+
+
+def test_long_seq_bf16_full_size():
+    """B=1, H=32, N=16384, d=128 bf16 with K x3 at full size; sampled rows from 6 heads."""
+    w = si.LONG_SEQ_BF16
+    say("long_seq: generating inputs")
+    q, k, v = si.workload_inputs(w)
+    say("long_seq: running fa_fwd")
+    o, m, l = run_case(q, k, v, "bf16", w.scale)
+    heads = [(0, 0), (0, 7), (0, 13), (0, 20), (0, 26), (0, 31)]
+    qb = lambda b, h: si.bf16_bits_to_f32(q.data[b, h]).astype(np.float64)
+    kb = lambda b, h: si.bf16_bits_to_f32(k.data[b, h]).astype(np.float64)
+    vb = lambda b, h: si.bf16_bits_to_f32(v.data[b, h]).astype(np.float64)
+    got, ref, gm, gl, rm, rl, bd = _sampled_rows(w, o, m, l, qb, kb, vb, heads, 128, 4)
+    say(f"long_seq: errors {errors(got, ref)}")
+    assert_close(got, ref, "bf16", "long seq sampled rows")
+    assert_stats(gm, gl, rm, rl, bd, "long seq")
+    assert np.all(np.isfinite(o))
+
+
+# ---------------------------------------------------------------------------------------------
+# split-KV partial states and their merge
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("shape", [(2, 3, 1, 1000, 128, 16), (1, 2, 3, 777, 64, 5), (1, 1, 40, 900, 64, 7),
+                                   (1, 2, 300, 700, 128, 3)], ids=lambda s: "x".join(map(str, s)))
+def test_split_states_and_merge_orders(dtype, shape):
+    B, H, Nq, Nk, d, S = shape
+    say(f"split dtype={dtype} shape={shape}")
+    q, k, v = si.small_case(300 + Nk, B, H, Nq, Nk, d, dtype)
+    scale = si.fp32_inverse_sqrt(d)
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    pm, pl, po = fa.fwd_split(qd, kd, vd, S, scale=scale)
+    torch.cuda.synchronize()
+    pm, pl, po = si.torch_to_f64(pm), si.torch_to_f64(pl), si.torch_to_f64(po)
+    qf, kf, vf = q.as_f64(), k.as_f64(), v.as_f64()
+    for b in range(B):
+        for h in range(H):
+            states = oracle.split_partial_states(qf[b, h], kf[b, h], vf[b, h], scale, S)
+            for c, (m_ref, l_ref, o_ref) in enumerate(states):
+                # each part: its m, and its normalised output o / l, equal the part's own attention
+                lo, hi = oracle.split_bounds(Nk, S)[c]
+                bound = stat_bound(qf[b, h], kf[b, h, lo:hi], scale)
+                assert np.all(np.abs(pm[c, b, h] - m_ref) <= bound)
+                # l and o are relative to the kernel's m; rebase to the oracle's m before comparing
+                w_ = np.exp(pm[c, b, h] - m_ref)
+                assert np.all(np.abs(pl[c, b, h] * w_ / l_ref - 1) <= 2 * bound)
+                assert_close(po[c, b, h] / pl[c, b, h][:, None], o_ref / l_ref[:, None], dtype, f"part {c}")
+    ref = oracle.attention_fp64(qf, kf, vf, scale)
+    outs = []
+    perm = si.merge_order(5, S)
+    for order in (None, perm, list(range(S))[::-1]):
+        o, m, l = fa.merge_states(*[torch.from_numpy(x.astype(np.float32)).to(DEV) for x in (pm, pl, po)],
+                                  order=order, return_stats=True)
+        torch.cuda.synchronize()
+        o = si.torch_to_f64(o)
+        assert_close(o, ref, dtype, f"merged order={order}")
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 1e-5
+
+
+def test_decode_bf16_full_size_split16_shuffled_merge():
+    """B=16, H=32, one query, Nk=32768, d=128 bf16; 16 splits merged in default_rng(5).permutation(16) order."""
+    w = si.DECODE_BF16
+    say("decode: generating inputs on the device")
+    q, k, v = si.decode_inputs_device(w, DEV)
+    say("decode: split + merge")
+    order = si.merge_order(w.seed, w.num_splits)
+    pm, pl, po = fa.fwd_split(q, k, v, w.num_splits, scale=w.scale)
+    o, m, l = fa.merge_states(pm, pl, po, order=order, return_stats=True)
+    o_seq = fa.merge_states(pm, pl, po)
+    torch.cuda.synchronize()
+    o, m, l, o_seq = (si.torch_to_f64(x) for x in (o, m, l, o_seq))
+    assert np.all(np.isfinite(o))
+    assert np.max(np.abs(o - o_seq)) < 1e-5
+    rng = np.random.default_rng(55)
+    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 12), rng.integers(0, w.H, 12))]
+    got, ref, gm, gl, rm, rl, bd = [], [], [], [], [], [], []
+    for b, h in heads:
+        qh, kh, vh = (si.torch_to_f64(x[b, h]) for x in (q, k, v))
+        o_ref, m_ref, l_ref = oracle.attention_rows_fp64(qh, kh, vh, w.scale)
+        got.append(o[b, h]); ref.append(o_ref); gm.append(m[b, h]); gl.append(l[b, h]); rm.append(m_ref); rl.append(l_ref)
+        bd.append(stat_bound(qh, kh, w.scale))
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    say(f"decode: errors {errors(got, ref)}")
+    assert_close(got, ref, "bf16", "decode sampled heads")
+    assert_stats(np.concatenate(gm), np.concatenate(gl), np.concatenate(rm), np.concatenate(rl), np.concatenate(bd),
+                 "decode")
+    # fa_fwd (one launch, no split) agrees with split + merge
+    o_full = si.torch_to_f64(fa.fwd(q, k, v, scale=w.scale))
+    assert np.max(np.abs(o_full - o)) < 1e-4
