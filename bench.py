@@ -30,6 +30,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="headline", choices=["headline", "long_seq", "decode"])
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
+                        "reference dispatch that scales the HBM byte counters of a profiling run")
     return p.parse_args()
 
 
@@ -106,6 +109,14 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        n_el = args.copy_calibration * 2 ** 20 // 4
+        src = torch.ones(n_el, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "decode":
         S = wl.num_splits
         pm = torch.empty((S, wl.B, wl.H, wl.Nq), device=dev, dtype=torch.float32)
@@ -178,7 +189,7 @@ def main():
     result["wall_s_timed"] = wall
 
     if not args.no_cpu and args.workload == "headline":
-        base, check = cpu_baseline(wl, q, k, v, o, max_heads=8)
+        base, check = cpu_baseline(wl, q, k, v, o, max_heads=wl.B * wl.H)
         result["cpu_baseline"] = base
         result["parity_sample"] = check
     print(json.dumps(result), flush=True)
