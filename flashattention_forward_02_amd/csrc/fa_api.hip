@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "fa.h"
@@ -50,6 +51,19 @@ fa_status check_common(const char* fn, const void* q, const void* k, const void*
   return FA_OK;
 }
 
+// Base-2 growth of the running max tolerated before the matrix-core kernel rescales its state
+// (see fwd_mfma.hip). 8 keeps every p below 2^8; FA_RESCALE_THRESHOLD (read once, for tests)
+// can set it, e.g. 0 to rescale whenever the max grows.
+float rescale_threshold() {
+  static const float tau = [] {
+    const char* e = getenv("FA_RESCALE_THRESHOLD");
+    if (!e || !*e) return 8.0f;
+    const float v = strtof(e, nullptr);
+    return (v >= 0.f && v <= 16.f) ? v : 8.0f;
+  }();
+  return tau;
+}
+
 fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, float scale) {
   fa::FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -63,6 +77,7 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H,
   a.num_splits = 1;
   a.scale = scale;
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.rescale_threshold = rescale_threshold();
   return a;
 }
 

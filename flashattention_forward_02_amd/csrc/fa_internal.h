@@ -27,6 +27,7 @@ struct FwdArgs {
   int out_dtype;    // Dtype of o (full mode)
   float scale;      // softmax scale applied to q.k (natural-log units)
   float scale_log2e;  // scale * log2(e): scores in base-2 units for exp2
+  float rescale_threshold;  // log2 units; see fwd_mfma.hip (0 = rescale whenever the max grows)
 };
 
 // Merge arguments. The merge order travels inside the kernel arguments.

@@ -328,3 +328,39 @@ def test_decode_bf16_full_size_split16_shuffled_merge():
     # fa_fwd (one launch, no split) agrees with split + merge
     o_full = si.torch_to_f64(fa.fwd(q, k, v, scale=w.scale))
     assert np.max(np.abs(o_full - o)) < 1e-4
+
+
+# ---------------------------------------------------------------------------------------------
+# the rescale threshold: 0 is the pages' recurrence literally; the default defers rescaling
+# ---------------------------------------------------------------------------------------------
+
+_THRESHOLD_SCRIPT = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, %(root)r)
+import flashattention_forward_02_amd as fa, oracle, seeded_inputs as si
+from tests._parity import assert_close, assert_stats, stat_bound
+for (B, H, Nq, Nk, d, kmul) in [(1, 2, 300, 1000, 64, 1.0), (1, 1, 256, 2000, 128, 3.0)]:
+    q, k, v = si.small_case(900 + Nk, B, H, Nq, Nk, d, "bf16", k_mult=kmul)
+    sc = si.fp32_inverse_sqrt(d)
+    o, m, l = fa.fwd(q.to_torch("cuda"), k.to_torch("cuda"), v.to_torch("cuda"), scale=sc, return_stats=True)
+    torch.cuda.synchronize()
+    ref, mr, lr = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), sc, return_stats=True)
+    assert_close(si.torch_to_f64(o), ref, "bf16", "threshold run")
+    assert_stats(si.torch_to_f64(m), si.torch_to_f64(l), mr, lr, stat_bound(q.as_f64(), k.as_f64(), sc))
+    np.save(%(out)r + "_%%d.npy" %% d, si.torch_to_f64(o))
+print("ok", flush=True)
+"""
+
+
+@pytest.mark.parametrize("threshold", ["0", "8"])
+def test_rescale_threshold_exact_and_deferred(threshold, tmp_path):
+    """Both the literal recurrence (threshold 0: rescale whenever the max grows) and the deferred one
+    match the oracle, in a fresh process that sets FA_RESCALE_THRESHOLD."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = str(tmp_path / f"o_{threshold}")
+    env = dict(os.environ, FA_RESCALE_THRESHOLD=threshold)
+    r = subprocess.run([sys.executable, "-c", _THRESHOLD_SCRIPT % {"root": root, "out": out}], env=env,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
