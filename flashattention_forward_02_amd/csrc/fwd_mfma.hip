@@ -2,12 +2,21 @@
 //
 // What is computed ("FlashAttention 简化版：Tiling + Online Softmax", §2.3 and §3.1): one
 // workgroup owns a tile of query rows of one (b, h) and streams that head's keys past it in
-// tiles of BC keys. Per query row it keeps a running maximum, the running sum l and the fp32
+// tiles of 64 keys. Per query row it keeps a running maximum, the running sum l and the fp32
 // output accumulator; each key tile computes the scores, adds exp(s - m) to l and exp(s - m) V
 // to the accumulator, and when the maximum grows, first scales l and the accumulator by
 // exp(m_old - m_new). The accumulator is divided by l once at the end.
 //
 // How it maps onto CDNA4:
+//  * Two wave groups in opposite phases. A CDNA SIMD overlaps matrix-core and VALU work only
+//    across different waves: one wave's MFMAs run while another wave issues VALU instructions
+//    (a probe of one wave interleaving independent MFMA and VALU instructions showed no
+//    overlap at all). A workgroup therefore has 8 waves, two per SIMD: group A (waves 0-3)
+//    and group B (waves 4-7), each owning its own query rows. Every tile is two phases per
+//    wave -- an MFMA phase (PV of the previous tile, then S of this tile) and a VALU phase
+//    (the softmax update of this tile) -- and group B runs one phase behind group A, with a
+//    workgroup barrier between phases. So at any time one wave of each SIMD is on the matrix
+//    core while the other is on the VALU.
 //  * Transposed products. S^T = K Q^T and O^T = V^T P^T, each as 32x32x16 MFMAs. In the
 //    32x32 accumulator layout a lane owns one column and 16 rows; with queries as columns a
 //    lane holds 16 scores of ONE query (rows = keys) and 16 output dims of that same query.
@@ -19,12 +28,14 @@
 //    permutation by ds_read_b64_tr_b16 (gfx950's transposing LDS read), so V stays row-major
 //    in LDS and is transposed on the way into registers.
 //  * K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4: no staging registers,
-//    no LDS write instructions), double-buffered: the loads of tile j+1 are issued before the
-//    MFMAs of tile j; one wait + barrier per tile. Both tiles are XOR-swizzled in 16-byte
-//    chunks so the MFMA operand reads spread over the LDS banks (K: chunk ^ (row % 8) for the
-//    row-per-lane 16-byte reads; V: chunk ^ 2*(row % 4) for the 4-row x 32-byte pattern of one
-//    transposing read). The swizzle is applied on the global side: the lane that fills LDS
-//    chunk (row, c) fetches global chunk (row, c ^ f(row)).
+//    no LDS write instructions), two buffers each, issued by group A. At d = 128 the loads of
+//    K(t+1) and V(t) start in A's VALU phase of tile t (no LDS reads there, so no MFMA phase
+//    stalls on them). At d = 64 they start in A's MFMA phase and A's VALU phase re-lays the raw
+//    V tile in LDS as ready-made PV operand fragments, so the MFMA phase reads V^T with plain
+//    16-byte reads instead of transposing ones. Both tiles are XOR-swizzled in 16-byte chunks
+//    (K: chunk ^ row % 8, V: chunk ^ 2 * (row % 4), picked by timing on gfx950) so the operand
+//    reads spread over the LDS banks. The swizzle is applied on the global side: the lane that
+//    fills LDS chunk (row, c) fetches global chunk (row, c ^ f(row)).
 //  * Scores are handled in base 2: with c = scale * log2(e), exp(s - m) = 2^(raw*c - m*c),
 //    one FMA and one v_exp_f32 per score. The true running max is kept on the raw dot
 //    products (scale >= 0, so max commutes with the scale) and m_out = scale * max.
@@ -35,13 +46,13 @@
 //    the reference (the identity of §2.2), the result is the same up to rounding. With a
 //    threshold of 0 this is the pages' recurrence literally (rescale whenever the max grows).
 //    At the end l (and, for split states, o) are re-expressed relative to the true maximum.
-//    The rescale is a wave-uniform branch, so tiles where no row of a wave needs it skip the
-//    D multiplies per row entirely.
+//    Calls that want no row statistics skip the running max altogether: the reference only
+//    moves when a tile's row sum of 2^(raw*c - m_ref) leaves [0, 2^threshold] (the first
+//    tile always does), which bounds every p the same way.
 //  * P is rounded to the input type (round to nearest even) only as the PV operand; l sums
 //    the fp32 values ("CS349E 第 11 讲 01_online_softmax.py", demo 4).
-//  * Four waves per workgroup, 64 query rows per wave (two 32-column MFMA blocks share every
-//    K/V operand read from LDS), 256 query rows per workgroup. Only the last key tile of a
-//    range can be partial; it runs a separate instantiation of the tile body that masks.
+//  * Query rows per wave: 64 at d = 64 (two 32-column MFMA blocks share every K/V operand read
+//    from LDS), 32 at d = 128 (the accumulator doubles); 512 or 256 rows per workgroup.
 
 #include "fa_internal.h"
 
@@ -72,11 +83,9 @@ template <> struct Mma<_Float16> {
   }
 };
 
-constexpr int kWaves = 4;
-constexpr int kNB = 2;                       // 32-query MFMA column blocks per wave
-constexpr int kBC = 64;                      // keys per tile
-constexpr int kBR = kWaves * kNB * 32;       // query rows per workgroup
+constexpr int kWaves = 8;                    // two groups of four, one wave of each per SIMD
 constexpr int kThreads = kWaves * 64;
+constexpr int kBC = 64;                      // keys per tile
 
 // Max / sum of a value and its counterpart in the other half of the wave (lane l and l ^ 32).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -105,40 +114,67 @@ __device__ __forceinline__ void store4(void* base, size_t elem, int out_dtype, f
   }
 }
 
+// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes land at lds + 16 * i. (A plain
+// function, not a template: the host compile pass rejects this target builtin inside templates.)
+__device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
 template <int D, typename T>
-struct Tile {
+struct Cfg {
   typedef typename Mma<T>::v8 v8;
-  static constexpr int KS = D / 16;                 // 16-wide k steps of S^T = K Q^T
-  static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  static constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
-  static constexpr int ELEMS = kBC * D;             // elements per K (or V) tile
-  static constexpr int CPW = ELEMS / 8 / kWaves;    // 16-byte chunks each wave moves per tensor
-  static constexpr int LPW = CPW / 64;              // direct-to-LDS loads per wave per tensor
-  static_assert(LPW >= 1 && LPW * 64 * kWaves * 8 == ELEMS, "tile / wave mismatch");
+  static constexpr int NB = (D <= 64) ? 2 : 1;     // 32-query MFMA column blocks per wave
+  static constexpr int BR = kWaves * NB * 32;      // query rows per workgroup
+  static constexpr int KS = D / 16;                // 16-wide k steps of S^T = K Q^T
+  static constexpr int DB = D / 32;                // 32-row blocks of O^T
+  static constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
+  static constexpr int ELEMS = kBC * D;            // elements per K (or V) tile
+  static constexpr int CPW = ELEMS / 8 / 4;        // 16-byte chunks each group-A wave moves per tensor
+  static constexpr int LPW = CPW / 64;             // direct-to-LDS loads per group-A wave per tensor
+  static_assert(LPW >= 1 && LPW * 64 * 4 * 8 == ELEMS, "tile / wave mismatch");
 };
 
-// Per-wave state of the online softmax for its 2 x 32 query rows (one value per lane each).
+// Online-softmax state of one wave's query rows (one value per lane each).
+template <int NB>
 struct RowState {
-  float mraw[kNB];   // true running max of the raw dot products
-  float m2ref[kNB];  // exponent reference, base-2 units
-  float lsum[kNB];   // sum of 2^(raw*c - m2ref)
+  float mraw[NB];   // true running max of the raw dot products (exact-max form only)
+  float m2ref[NB];  // exponent reference, base-2 units
+  float lsum[NB];   // sum of 2^(raw*c - m2ref)
 };
 
-// One key tile: S^T MFMAs, online-softmax update, PV MFMAs. TAIL masks keys >= valid.
-template <int D, typename T, bool TAIL>
-__device__ __forceinline__ void tile_step(const T* __restrict__ lk, const T* __restrict__ lv,
-                                          const typename Tile<D, T>::v8 (&qf)[kNB][Tile<D, T>::KS],
-                                          f32x16_t (&acc)[kNB][Tile<D, T>::DB], RowState& st, bool first,
-                                          int valid, float c2, float tau, int lane) {
-  typedef Tile<D, T> C;
+// XOR swizzles of the 16-byte chunks of LDS row r: chunk c of a K row is stored at c ^ swzk(r),
+// of a V row at c ^ swzv(r). Picked by timing the kernel under several swizzles on gfx950: the
+// K tile is read one row per lane, 16 bytes at a time; the V tile by transposing reads of
+// 4 rows x 8 bytes per 16-lane group.
+__device__ __forceinline__ int swzk(int r) { return (r & 7); }
+__device__ __forceinline__ int swzv(int r) { return ((r & 3) << 1); }
+
+// HBM -> LDS of one 64-row K or V tile, one quarter per group-A wave (gw = 0..3). Rows past
+// `kend` repeat the last key of the range; their scores are masked.
+template <int D, typename T, bool KT>
+__device__ __forceinline__ void load_tile2(const T* __restrict__ X, T* lx, int key0, int kend, int gw, int lane) {
+  typedef Cfg<D, T> C;
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int base = gw * C::CPW + i * 64;  // first LDS chunk of this load (wave-uniform)
+    const int ci = base + lane;
+    const int r = ci / C::CH, cpos = ci % C::CH;
+    const int key = min(key0 + r, kend - 1);
+    const int gch = cpos ^ (KT ? swzk(r) : swzv(r));
+    global_to_lds16(X + (size_t)key * D + (gch << 3), &lx[base * 8]);
+  }
+}
+
+// S^T = K Q^T for one tile: rows = 64 keys (two 32-blocks), columns = this wave's queries.
+template <int D, typename T>
+__device__ __forceinline__ void s_tile(const T* __restrict__ lk, const typename Cfg<D, T>::v8 (&qf)[Cfg<D, T>::NB][Cfg<D, T>::KS],
+                                       f32x16_t (&s)[Cfg<D, T>::NB][2], int lane) {
+  typedef Cfg<D, T> C;
   typedef typename C::v8 v8;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-
-  // ---- S^T = K Q^T : rows = 64 keys (two 32-blocks), columns = this wave's queries ----
-  f32x16_t s[kNB][2];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb)
+  for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -149,70 +185,20 @@ __device__ __forceinline__ void tile_step(const T* __restrict__ lk, const T* __r
     for (int kb = 0; kb < 2; ++kb) {
       const int r = kb * 32 + l32;
       const int ch = ks * 2 + hf;
-      const v8 kf = *reinterpret_cast<const v8*>(&lk[r * D + ((ch ^ (r & 7)) << 3)]);
+      const v8 kf = *reinterpret_cast<const v8*>(&lk[r * D + ((ch ^ swzk(r)) << 3)]);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) s[nb][kb] = Mma<T>::mma(kf, qf[nb][ks], s[nb][kb]);
+      for (int nb = 0; nb < C::NB; ++nb) s[nb][kb] = Mma<T>::mma(kf, qf[nb][ks], s[nb][kb]);
     }
   }
+}
 
-  if constexpr (TAIL) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key >= valid) {
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) s[nb][kb][r] = -INFINITY;
-        }
-      }
-  }
-
-  // ---- online softmax ----
-  v8 pf[kNB][4];  // PV B operands, one per 16-key step
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    float mx = s[nb][0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][kb][r]);
-    mx = xhalf_max(mx);
-    st.mraw[nb] = fmaxf(st.mraw[nb], mx);
-    const float mx2 = mx * c2;
-    const bool need = first || (mx2 > st.m2ref[nb] + tau);
-    if (__ballot(need)) {  // wave-uniform: some row of this wave moves its reference
-      const float ref = need ? mx2 : st.m2ref[nb];
-      if (!first) {
-        const float alpha = __builtin_amdgcn_exp2f(st.m2ref[nb] - ref);
-        st.lsum[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nb][db][r] *= alpha;
-      }
-      st.m2ref[nb] = ref;
-    }
-    const float nref = -st.m2ref[nb];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int r = half * 8 + u;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][kb][r], c2, nref));
-          if constexpr (TAIL) {
-            if (s[nb][kb][r] == -INFINITY) p = 0.f;
-          }
-          rs += p;
-          pf[nb][kb * 2 + half][u] = (T)p;
-        }
-    st.lsum[nb] += xhalf_sum(rs);
-  }
-
-  // ---- O^T += V^T P^T : 16 keys per step, V^T read transposed from row-major LDS ----
+// O^T += V^T P^T for one tile: 16 keys per MFMA step, V^T read transposed from row-major LDS.
+template <int D, typename T>
+__device__ __forceinline__ void pv_tile(const T* __restrict__ lv, const typename Cfg<D, T>::v8 (&pf)[Cfg<D, T>::NB][4],
+                                        f32x16_t (&acc)[Cfg<D, T>::NB][Cfg<D, T>::DB], int lane) {
+  typedef Cfg<D, T> C;
+  typedef typename C::v8 v8;
+  const int hf = lane >> 5;
   const int tj = lane & 15;
   const int ti = tj >> 2;
   const int tq = tj & 3;
@@ -223,49 +209,157 @@ __device__ __forceinline__ void tile_step(const T* __restrict__ lk, const T* __r
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int col = db * 32 + tgb * 16 + tq * 4;
-      const int off1 = row1 * D + (((col >> 3) ^ (ti << 1)) << 3) + (col & 7);
-      const int off2 = off1 + 8 * D;
+      const int off1 = row1 * D + (((col >> 3) ^ swzv(row1)) << 3) + (col & 7);
+      const int off2 = (row1 + 8) * D + (((col >> 3) ^ swzv(row1 + 8)) << 3) + (col & 7);
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lv[off1]);
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lv[off2]);
       const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
       const u32x4_t packed = {lo2[0], lo2[1], hi2[0], hi2[1]};
       const v8 vf = __builtin_bit_cast(v8, packed);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[nb][db] = Mma<T>::mma(vf, pf[nb][g], acc[nb][db]);
+      for (int nb = 0; nb < C::NB; ++nb) acc[nb][db] = Mma<T>::mma(vf, pf[nb][g], acc[nb][db]);
     }
   }
 }
 
-// HBM -> LDS of one K/V tile (keys key0 .. key0 + 63), swizzled as described at the top. Rows
-// past `kend` repeat the last key of the range; their scores are masked by the tail tile.
+// Stage V(t) as ready-made MFMA A operands: fragment (g, db) of a tile is the 16 bytes every
+// lane feeds the PV MFMA of 16-key step g and 32-dim block db -- V^T[dim][keys of step g] in the
+// key order of the P operand -- stored lane after lane, so each wave later reads it with one
+// conflict-free 16-byte read. The transposition itself (two ds_read_b64_tr_b16 per fragment)
+// happens once per workgroup and tile instead of once per wave. Group-A wave gw stages
+// fragments gw, gw + 4, ...
 template <int D, typename T>
-__device__ __forceinline__ void load_kv_tile(const T* __restrict__ K, const T* __restrict__ V, T* lk, T* lv, int key0,
-                                             int kend, int wave, int lane) {
-  typedef Tile<D, T> C;
+__device__ __forceinline__ void stage_v(const T* __restrict__ lv, T* vfrag, int gw, int lane) {
+  constexpr int DB = D / 32;
+  const int hf = lane >> 5;
+  const int tj = lane & 15;
+  const int ti = tj >> 2;
+  const int tq = tj & 3;
+  const int tgb = (lane >> 4) & 1;
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int base = wave * C::CPW + i * 64;  // first LDS chunk of this load (wave-uniform)
-    const int ci = base + lane;
-    const int r = ci / C::CH, cpos = ci % C::CH;
-    const int key = min(key0 + r, kend - 1);
-    const T* gk = K + (size_t)key * D + ((cpos ^ (r & 7)) << 3);
-    const T* gv = V + (size_t)key * D + ((cpos ^ ((r & 3) << 1)) << 3);
-    __builtin_amdgcn_global_load_lds(gk, (lds_void_t*)&lk[base * 8], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gv, (lds_void_t*)&lv[base * 8], 16, 0, 0);
+  for (int f = gw; f < (kBC / 16) * DB; f += 4) {
+    const int g = f / DB, db = f % DB;
+    const int row1 = 16 * g + 4 * hf + ti;
+    const int col = db * 32 + tgb * 16 + tq * 4;
+    const int off1 = row1 * D + (((col >> 3) ^ swzv(row1)) << 3) + (col & 7);
+    const int off2 = (row1 + 8) * D + (((col >> 3) ^ swzv(row1 + 8)) << 3) + (col & 7);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lv[off1]);
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lv[off2]);
+    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+    const u32x4_t packed = {lo2[0], lo2[1], hi2[0], hi2[1]};
+    *reinterpret_cast<u32x4_t*>(&vfrag[(f * 64 + lane) * 8]) = packed;
   }
 }
 
-// Workgroups per CU the register budget is sized for: two 4-wave workgroups (2 waves per SIMD,
-// 256 registers each) at d = 64, one at d = 128 (512 registers, the accumulator alone is 128).
-template <int D> struct Occupancy { static constexpr int kMinBlocks = (D <= 64) ? 2 : 1; };
-
-template <int D, typename T, int MINB = Occupancy<D>::kMinBlocks>
-__global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int n_qtiles) {
-  typedef Tile<D, T> C;
+// O^T += V^T P^T for one tile from staged fragments: one 16-byte LDS read per MFMA A operand.
+template <int D, typename T>
+__device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typename Cfg<D, T>::v8 (&pf)[Cfg<D, T>::NB][4],
+                                          f32x16_t (&acc)[Cfg<D, T>::NB][Cfg<D, T>::DB], int lane) {
+  typedef Cfg<D, T> C;
   typedef typename C::v8 v8;
+#pragma unroll
+  for (int g = 0; g < kBC / 16; ++g)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const v8 vf = *reinterpret_cast<const v8*>(&vfrag[((g * C::DB + db) * 64 + lane) * 8]);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[nb][db] = Mma<T>::mma(vf, pf[nb][g], acc[nb][db]);
+    }
+}
 
+// Softmax update of one tile for one 32-query block, given the tile scores s (raw dot
+// products) of that block: moves the exponent reference when needed (scaling l and the block's
+// accumulator), writes P as PV operands and adds its row sum to l.
+//   FAST = false: exact running max, reference moves when the tile max exceeds it by > tau.
+//   FAST = true:  no running max; reference moves when the tile's row sum leaves [0, 2^tau].
+template <int D, typename T, bool TAIL>
+__device__ __forceinline__ float exps_block(const f32x16_t (&s)[2], float ref, float c2, float (&p)[32]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 4][i & 15], c2, -ref));
+    if constexpr (TAIL) {
+      if (s[i >> 4][i & 15] == -INFINITY) x = 0.f;
+    }
+    p[i] = x;
+    rs += x;
+  }
+  return xhalf_sum(rs);
+}
+
+__device__ __forceinline__ float max_block(const f32x16_t (&s)[2]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+  return xhalf_max(mx);
+}
+
+// Move the exponent reference of the rows with `need` to `target`, scaling l and the block's
+// accumulator by 2^(ref_old - ref_new). Wave-uniform branch: only some tiles move some rows.
+template <int D>
+__device__ __forceinline__ bool move_ref(bool need, float target, bool first, float& m2ref, float& lsum,
+                                         f32x16_t (&acc)[D / 32]) {
+  if (__ballot(need)) {
+    asm volatile("" ::: "memory");
+    const float ref = need ? target : m2ref;
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(m2ref - ref);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    m2ref = ref;
+    return true;
+  }
+  return false;
+}
+
+// Softmax update of one tile for one 32-query block, given the tile scores s (raw dot
+// products) of that block: moves the exponent reference when needed (scaling l and the block's
+// accumulator), writes P as PV operands and adds its row sum to l.
+//   FAST = false: exact running max, reference moves when the tile max exceeds it by > tau.
+//   FAST = true:  no running max; reference moves when the tile's row sum leaves [0, 2^tau].
+template <int D, typename T, bool FAST, bool TAIL>
+__device__ __forceinline__ void softmax_block(const f32x16_t (&s)[2], float& mraw, float& m2ref, float& lsum,
+                                              typename Cfg<D, T>::v8 (&pf)[4], f32x16_t (&acc)[Cfg<D, T>::DB],
+                                              bool first, float c2, float tau, float bound) {
+  float p[32];
+  float rs;
+  if constexpr (FAST) {
+    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p);
+    const bool trig = first || !(rs <= bound);
+    if (__ballot(trig)) {
+      const float mx2 = max_block(s) * c2;
+      if (move_ref<D>(trig, first ? mx2 : fmaxf(m2ref, mx2), first, m2ref, lsum, acc))
+        rs = exps_block<D, T, TAIL>(s, m2ref, c2, p);
+    }
+  } else {
+    const float mx = max_block(s);
+    mraw = fmaxf(mraw, mx);
+    const float mx2 = mx * c2;
+    move_ref<D>(first || (mx2 > m2ref + tau), mx2, first, m2ref, lsum, acc);
+    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p);
+  }
+  lsum += rs;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) pf[i >> 3][i & 7] = (T)p[i];
+}
+
+template <int D, typename T, bool FAST>
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_qtiles) {
+  typedef Cfg<D, T> C;
+  typedef typename C::v8 v8;
+  constexpr int NB = C::NB;
+
+  // At d = 64 group A also re-lays each V tile as ready-made PV operand fragments (see stage_v):
+  // its VALU phase has room for it, and it takes the transposing reads off the MFMA phase. At
+  // d = 128 the softmax phase is the shorter one and the plain transposing reads measured faster.
+  constexpr bool STAGE = D == 64;
   __shared__ __attribute__((aligned(16))) T lds_k[2][C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v[2][C::ELEMS];                          // raw V tiles
+  __shared__ __attribute__((aligned(16))) T lds_vf[STAGE ? 2 : 1][STAGE ? C::ELEMS : 8];  // staged fragments
 
   // ---- work item: (query tile, split, h, b) ----
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -282,19 +376,22 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
   const int kbeg = split_begin(split, a.Nk, a.num_splits);
   const int kend = split_begin(split + 1, a.Nk, a.num_splits);
   const int nkeys = kend - kbeg;
-  const int ntiles = (nkeys + kBC - 1) / kBC;
+  const int T_ = (nkeys + kBC - 1) / kBC;         // key tiles (>= 1)
+  const int last_valid = nkeys - (T_ - 1) * kBC;  // keys in the last tile (1..64)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool group_a = wave < 4;
+  const int gw = wave & 3;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int qrow0 = qt * kBR + wave * (kNB * 32);
+  const int qrow0 = qt * C::BR + wave * (NB * 32);
 
   // ---- Q^T fragments: B operand of S^T = K Q^T, lane = query column, 8 dims per lane ----
-  v8 qf[kNB][C::KS];
+  v8 qf[NB][C::KS];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int row = qrow0 + nb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -304,16 +401,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
     }
   }
 
-  auto load_tile = [&](int t, int buf) {
-    load_kv_tile<D, T>(K, V, lds_k[buf], lds_v[buf], kbeg + t * kBC, kend, wave, lane);
-  };
-
   const float c2 = a.scale_log2e;
   const float tau = a.rescale_threshold;
-  RowState st;
-  f32x16_t acc[kNB][C::DB];
+  const float bound = __builtin_amdgcn_exp2f(tau);
+  RowState<NB> st;
+  f32x16_t acc[NB][C::DB];
+  f32x16_t s[NB][2];
+  v8 pf[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     st.mraw[nb] = -INFINITY;
     st.m2ref[nb] = 0.f;
     st.lsum[nb] = 0.f;
@@ -323,31 +419,98 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
       for (int r = 0; r < 16; ++r) acc[nb][db][r] = 0.f;
   }
 
-  if (ntiles > 0) load_tile(0, 0);
+  // ---- the two phases of one tile ----
+  // Loads (group A only; global -> LDS, asynchronous). Staged: K(t+1) and V(t+1) start at the top
+  // of the MFMA phase of tile t. Otherwise K(t+1) and V(t) start at the top of the VALU phase of
+  // tile t, which reads no LDS, so the MFMA phase never waits on an outstanding load. Either way
+  // group A waits for them at the end of its VALU phase, and no wave reads a buffer before the
+  // barrier that follows, nor while a load into it is in flight (every buffer's previous
+  // contents were last read at least one barrier earlier).
+  auto phase_mfma = [&](int t, bool do_pv, bool do_s) {
+    if constexpr (STAGE) {
+      if (group_a && t + 1 < T_) {
+        load_tile2<D, T, true>(K, lds_k[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane);
+        load_tile2<D, T, false>(V, lds_v[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane);
+      }
+      if (do_pv) pv_staged<D, T>(lds_vf[(t - 1) & 1], pf, acc, lane);
+    } else {
+      if (do_pv) pv_tile<D, T>(lds_v[(t - 1) & 1], pf, acc, lane);
+    }
+    if (do_s) s_tile<D, T>(lds_k[t & 1], qf, s, lane);
+    __syncthreads();
+  };
+  // VALU phase of tile t: (staged) group A re-lays V(t); the softmax update; group A waits for its
+  // loads; barrier.
+  auto valu_prologue = [&](int t) {
+    if constexpr (STAGE) {
+      if (group_a) stage_v<D, T>(lds_v[t & 1], lds_vf[t & 1], gw, lane);
+    } else if (group_a) {
+      if (t + 1 < T_) load_tile2<D, T, true>(K, lds_k[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane);
+      if (t < T_) load_tile2<D, T, false>(V, lds_v[t & 1], kbeg + t * kBC, kend, gw, lane);
+    }
+  };
+  auto phase_valu_full = [&](int t, bool first) {
+    valu_prologue(t);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      softmax_block<D, T, FAST, false>(s[nb], st.mraw[nb], st.m2ref[nb], st.lsum[nb], pf[nb], acc[nb], first, c2, tau,
+                                       bound);
+    if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  auto phase_valu_tail = [&](int t, bool first) {
+    valu_prologue(t);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= last_valid) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s[nb][kb][r] = -INFINITY;
+        }
+      }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      softmax_block<D, T, FAST, true>(s[nb], st.mraw[nb], st.m2ref[nb], st.lsum[nb], pf[nb], acc[nb], first, c2, tau,
+                                      bound);
+    if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // ---- prologue: K(0) (and, staged, V(0)) resident; group B then sits out one phase ----
+  if (group_a) {
+    load_tile2<D, T, true>(K, lds_k[0], kbeg, kend, gw, lane);
+    if constexpr (STAGE) load_tile2<D, T, false>(V, lds_v[0], kbeg, kend, gw, lane);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (!group_a) __syncthreads();
 
-  // Full tiles, then (outside the loop, so the loop body has one version) the partial last tile.
-  const int nfull = nkeys / kBC;
-  for (int t = 0; t < nfull; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
-    tile_step<D, T, false>(lds_k[buf], lds_v[buf], qf, acc, st, t == 0, kBC, c2, tau, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // First tile, full tiles, partial last tile, then the final PV; every tile is one MFMA phase
+  // and one VALU phase. Only the first and the last tile take the variants with the first-tile
+  // and masking logic, so the steady-state loop carries one softmax body.
+  const bool partial = last_valid < kBC;
+  phase_mfma(0, false, true);
+  if (T_ == 1 && partial) phase_valu_tail(0, true);
+  else phase_valu_full(0, true);
+  const int nfull = partial ? T_ - 1 : T_;
+  for (int t = 1; t < nfull; ++t) {
+    phase_mfma(t, true, true);
+    phase_valu_full(t, false);
   }
-  if (nfull < ntiles) {
-    const int buf = nfull & 1;
-    tile_step<D, T, true>(lds_k[buf], lds_v[buf], qf, acc, st, nfull == 0, nkeys - nfull * kBC, c2, tau, lane);
+  if (partial && T_ > 1) {
+    phase_mfma(T_ - 1, true, true);
+    phase_valu_tail(T_ - 1, false);
   }
+  phase_mfma(T_, true, false);
+  if (group_a) __syncthreads();
 
   // ---- epilogue: re-express l (and o) relative to the true maximum; O = acc / l ----
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int row = qrow0 + nb * 32 + l32;
     if (row >= a.Nq) continue;
-    const float to_true = __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
-    const float l_true = st.lsum[nb] * to_true;
     if (a.split_mode == 0) {
       const float inv = 1.f / st.lsum[nb];
       const size_t obase = (head * (size_t)a.Nq + row) * D;
@@ -359,11 +522,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
           store4(a.o, obase + dd, a.out_dtype, acc[nb][db][4 * g4] * inv, acc[nb][db][4 * g4 + 1] * inv,
                  acc[nb][db][4 * g4 + 2] * inv, acc[nb][db][4 * g4 + 3] * inv);
         }
-      if (hf == 0) {
-        if (a.m_out) a.m_out[head * a.Nq + row] = a.scale * st.mraw[nb];
-        if (a.l_out) a.l_out[head * a.Nq + row] = l_true;
+      if constexpr (!FAST) {
+        if (hf == 0) {
+          const float to_true = __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
+          if (a.m_out) a.m_out[head * a.Nq + row] = a.scale * st.mraw[nb];
+          if (a.l_out) a.l_out[head * a.Nq + row] = st.lsum[nb] * to_true;
+        }
       }
-    } else {
+    } else if constexpr (!FAST) {
+      const float to_true = __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
       const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -375,7 +542,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
         }
       if (hf == 0) {
         a.part_m[prow] = a.scale * st.mraw[nb];
-        a.part_l[prow] = l_true;
+        a.part_l[prow] = st.lsum[nb] * to_true;
       }
     }
   }
@@ -383,14 +550,19 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_mfma_kernel(FwdArgs a, int
 
 template <int D, typename T>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
-  const int n_qtiles = (a.Nq + kBR - 1) / kBR;
+  typedef Cfg<D, T> C;
+  const int n_qtiles = (a.Nq + C::BR - 1) / C::BR;
   const long long nwg = (long long)n_qtiles * a.num_splits * a.H * a.B;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   int nq = n_qtiles;
   void* kargs[] = {&args, &nq};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T>), dim3((unsigned)nwg), dim3(kThreads),
-                         kargs, 0, s);
+  // Full-output calls without row statistics take the sum-checked softmax; statistics, split
+  // states and a zero threshold (the literal recurrence) take the running-max form.
+  const bool fast = a.split_mode == 0 && !a.m_out && !a.l_out && a.rescale_threshold >= 1.f;
+  const void* k = fast ? reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, true>)
+                       : reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, false>);
+  return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
 }
 
 }  // namespace

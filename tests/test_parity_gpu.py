@@ -364,3 +364,75 @@ def test_rescale_threshold_exact_and_deferred(threshold, tmp_path):
     r = subprocess.run([sys.executable, "-c", _THRESHOLD_SCRIPT % {"root": root, "out": out}], env=env,
                        capture_output=True, text=True, timeout=110)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------------------------
+# calls without row statistics (the sum-checked softmax of the matrix-core kernel)
+# ---------------------------------------------------------------------------------------------
+
+def run_nostats(q, k, v, scale, out_dtype="f32"):
+    o = fa.fwd(q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV), scale=scale, out_dtype=_tdt(out_dtype))
+    torch.cuda.synchronize()
+    return si.torch_to_f64(o)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(2, 3, 300, 333, 64), (1, 1, 513, 1000, 128), (1, 2, 257, 64, 64),
+                                   (1, 1, 40, 17, 64), (2, 1, 64, 129, 128)], ids=lambda s: "x".join(map(str, s)))
+def test_no_stats_path(dtype, shape):
+    B, H, Nq, Nk, d = shape
+    q, k, v = si.small_case(4000 + Nq + Nk, B, H, Nq, Nk, d, dtype)
+    scale = si.fp32_inverse_sqrt(d)
+    o = run_nostats(q, k, v, scale)
+    ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale)
+    assert_close(o, ref, dtype, f"no-stats {dtype} {shape}")
+
+
+@pytest.mark.parametrize("kmul,shift", [(1.0, 0.0), (3.0, 0.0), (1.0, 100.0), (8.0, 0.0)])
+def test_no_stats_path_score_ranges(kmul, shift):
+    """Keys x3 and x8 (wide score ranges, so the reference moves on later tiles) and scores shifted
+    to about 100 (exponents far from 0 in every tile)."""
+    q, k, v = si.small_case(77, 1, 2, 300, 2000, 64, "bf16", k_mult=kmul)
+    qf = q.as_f64()
+    if shift:
+        u = qf[0, 0].mean(axis=0)
+        u = u * (shift / (0.125 * float(u @ u)))
+        k = si.encode((k.as_f64() + u).astype(np.float32), "bf16")
+    o = run_nostats(q, k, v, 0.125)
+    ref = oracle.attention_fp64(qf, k.as_f64(), v.as_f64(), 0.125)
+    assert_close(o, ref, "bf16", f"no-stats kmul={kmul} shift={shift}")
+
+
+def test_no_stats_increasing_scores_across_tiles():
+    """Scores that grow tile after tile (keys scaled up along the sequence) force the reference to move
+    many times; a late key far above every earlier one exercises the overflow guard."""
+    q, k, v = si.small_case(78, 1, 1, 256, 1024, 64, "bf16")
+    kf = k.as_f64()
+    ramp = np.linspace(0.1, 6.0, 1024)[None, None, :, None]
+    k2 = si.encode((kf * ramp).astype(np.float32), "bf16")
+    o = run_nostats(q, k2, v, 0.125)
+    ref = oracle.attention_fp64(q.as_f64(), k2.as_f64(), v.as_f64(), 0.125)
+    assert_close(o, ref, "bf16", "ramp")
+
+
+def test_no_stats_zero_scale():
+    q, k, v = si.small_case(5, 1, 2, 300, 130, 64, "bf16")
+    o = run_nostats(q, k, v, 0.0)
+    ref = np.broadcast_to(v.as_f64().mean(axis=2, keepdims=True), o.shape)
+    assert_close(o, ref, "bf16", "no-stats scale=0")
+
+
+def test_headline_bf16_full_size_no_stats():
+    """The benchmarked launch exactly (no statistics requested), sampled rows from 8 heads."""
+    w = si.HEADLINE_BF16
+    q, k, v = si.workload_inputs(w)
+    o = run_nostats(q, k, v, w.scale)
+    qf, kf, vf = q.as_f64(), k.as_f64(), v.as_f64()
+    rng = np.random.default_rng(33)
+    got, ref = [], []
+    for (b, h) in [(0, 1), (1, 7), (2, 14), (3, 3), (0, 9), (1, 0), (2, 5), (3, 12)]:
+        rows = np.sort(rng.choice(w.Nq, size=256, replace=False))
+        got.append(o[b, h, rows])
+        ref.append(oracle.attention_rows_fp64(qf[b, h, rows], kf[b, h], vf[b, h], w.scale)[0])
+    say(f"headline no-stats errors {errors(np.concatenate(got), np.concatenate(ref))}")
+    assert_close(np.concatenate(got), np.concatenate(ref), "bf16", "headline no-stats")
