@@ -29,12 +29,20 @@ What each function is pinned against (tests/test_oracle_pins.py):
 * ``fa1_order_attention`` -- the delayed-normalisation form.
 * ``round_to_bf16`` / ``round_to_f16`` -- torch's and numpy's casts; the
   relative P.V error magnitudes the lecture-11 demo 4 reports.
+* the causal mask (``attention_fp64(causal=True)``, ``causal_last_key``) -- literal
+  loops over the visible keys; torch's float64 attention with is_causal for Nq = Nk;
+  each row equals unmasked attention over its key prefix; Nq < Nk equals the last
+  rows of the square problem; masked split states merge to the masked result.
+* grouped K/V heads (``kv_head_of``, K/V with fewer heads than Q) -- the head map
+  written out; torch's float64 attention with enable_gqa; MHA on repeated K/V heads.
 
 Parity unpinned: nothing in this package. (The exact bf16 error of a GPU kernel
 depends on where its tiles fall and is bounded by the tolerance, not pinned.)
 """
 from .attention import (  # noqa: F401
     scores_fp64,
+    causal_last_key,
+    kv_head_of,
     attention_fp64,
     attention_rows_fp64,
     safe_softmax,

@@ -28,7 +28,7 @@ def scores_fp64(q, k, scale) -> np.ndarray:
     return float(scale) * (q @ k.T)
 
 
-def attention_rows_fp64(q, k, v, scale):
+def attention_rows_fp64(q, k, v, scale, last_key=None):
     """Full attention for one head: q [Nq, d], k [Nk, d], v [Nk, dv] -> (O [Nq, dv], m [Nq], l [Nq]).
 
     The three passes of the stored-row form ([CS349E-L11] ``attn_row_3pass``;
@@ -36,6 +36,11 @@ def attention_rows_fp64(q, k, v, scale):
     O = (sum_j p_j v_j) / l. ``m`` is the row maximum of the scaled scores and
     ``l`` the sum of exp(s_j - m) (the statistics [FA-Fill Exercise 5] keeps for
     the backward pass).
+
+    ``last_key`` (optional, one int per query row) restricts row i to the keys
+    j <= last_key[i]: the scores of the other keys are -inf, so they take no part
+    in m, p, l or O (the causal mask of [FA-Simplified §7]; see ``causal_last_key``).
+    Every row must keep at least one key.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -43,43 +48,93 @@ def attention_rows_fp64(q, k, v, scale):
     if k.shape[0] < 1:
         raise ValueError("softmax over an empty key set is undefined (Nk must be >= 1)")
     s = scores_fp64(q, k, scale)                 # pass 0: the whole score row is stored
+    if last_key is not None:
+        last_key = np.asarray(last_key).reshape(-1)
+        if last_key.shape[0] != q.shape[0] or np.any(last_key < 0):
+            raise ValueError("last_key needs one index >= 0 per query row")
+        s = np.where(np.arange(k.shape[0])[None, :] <= last_key[:, None], s, NEG_INF)
     m = s.max(axis=1)                            # pass 1: row maximum
-    p = np.exp(s - m[:, None])                   # pass 2: exponentials and their sum
+    p = np.exp(s - m[:, None])                   # pass 2: exponentials and their sum (exp(-inf) = 0)
     l = p.sum(axis=1)
     o = (p @ v) / l[:, None]                     # pass 3: normalise and weight V
     return o, m, l
 
 
-def attention_fp64(q, k, v, scale, row_block: int = 512, return_stats: bool = False):
-    """O = softmax(scale * Q K^T) V for [B, H, Nq, d] / [B, H, Nk, d] inputs (or any leading dims).
+def causal_last_key(rows, Nq: int, Nk: int) -> np.ndarray:
+    """Last key each query row may see under the causal mask: row i sees keys j <= i + (Nk - Nq).
+
+    [FA-Simplified §7] names the causal mask of decoder models (GPT) as the first
+    extension and gives no formula. For Nq = Nk this is the usual rule j <= i. For
+    Nq < Nk the queries are read as the last Nq positions of the Nk-long sequence
+    (a decoder attending to its cached keys), so the last query sees every key.
+    Nq > Nk would leave the first rows without keys and is rejected.
+    """
+    if Nq > Nk:
+        raise ValueError("the causal mask needs Nq <= Nk (every query row keeps at least one key)")
+    return np.asarray(rows, dtype=np.int64) + (Nk - Nq)
+
+
+def kv_head_of(h: int, H: int, H_kv: int) -> int:
+    """K/V head read by query head h when H query heads share H_kv K/V heads.
+
+    [FA-Simplified §7] names multi-query / grouped-query attention (MQA / GQA) as an
+    extension that cuts K/V memory, without a layout. Reading taken: consecutive
+    query heads form the groups, H / H_kv heads each, so head h reads K/V head
+    h // (H / H_kv); H_kv = H is ordinary multi-head attention and H_kv = 1 is MQA.
+    """
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"H={H} is not a multiple of H_kv={H_kv}")
+    return h // (H // H_kv)
+
+
+def attention_fp64(q, k, v, scale, row_block: int = 512, return_stats: bool = False, causal: bool = False):
+    """O = softmax(scale * Q K^T) V for [B, H, Nq, d] queries and [B, H_kv, Nk, d] keys and values.
 
     The result every kernel must reproduce ([FA-Simplified §3.1]: tiling does the
     same arithmetic as standard attention, only its rounding order differs;
     [FA-Simplified §4.1]). Rows are processed in blocks of ``row_block`` queries
     so no buffer exceeds [row_block, Nk] float64; that is a memory bound on this
     reference only and changes no arithmetic.
+
+    K and V may have fewer heads than Q (axis -3): query head h then reads K/V head
+    ``kv_head_of(h, H, H_kv)``. With ``causal`` row i sees the keys up to
+    ``causal_last_key(i, Nq, Nk)``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    lead = q.shape[:-2]
-    assert k.shape[:-2] == lead and v.shape[:-2] == lead, "Q, K, V leading dims differ"
+    if q.ndim == 2:
+        q, k, v = q[None], k[None], v[None]
+        squeeze = True
+    else:
+        squeeze = False
+    lead, H, H_kv = q.shape[:-3], q.shape[-3], k.shape[-3]
+    assert k.shape[:-3] == lead and v.shape[:-3] == lead, "Q, K, V leading dims differ"
+    assert v.shape[-3] == H_kv, "K and V head counts differ"
     Nq, Nk = q.shape[-2], k.shape[-2]
-    qf = q.reshape(-1, Nq, q.shape[-1])
-    kf = k.reshape(-1, Nk, k.shape[-1])
-    vf = v.reshape(-1, Nk, v.shape[-1])
-    out = np.empty((qf.shape[0], Nq, vf.shape[-1]))
-    ms = np.empty((qf.shape[0], Nq))
-    ls = np.empty((qf.shape[0], Nq))
-    for h in range(qf.shape[0]):
-        for r0 in range(0, Nq, row_block):
-            o, m, l = attention_rows_fp64(qf[h, r0:r0 + row_block], kf[h], vf[h], scale)
-            out[h, r0:r0 + row_block] = o
-            ms[h, r0:r0 + row_block] = m
-            ls[h, r0:r0 + row_block] = l
-    out = out.reshape(lead + (Nq, vf.shape[-1]))
+    qf = q.reshape((-1, H, Nq, q.shape[-1]))
+    kf = k.reshape((-1, H_kv, Nk, k.shape[-1]))
+    vf = v.reshape((-1, H_kv, Nk, v.shape[-1]))
+    out = np.empty((qf.shape[0], H, Nq, vf.shape[-1]))
+    ms = np.empty((qf.shape[0], H, Nq))
+    ls = np.empty((qf.shape[0], H, Nq))
+    for b in range(qf.shape[0]):
+        for h in range(H):
+            hk = kv_head_of(h, H, H_kv)
+            for r0 in range(0, Nq, row_block):
+                rows = np.arange(r0, min(Nq, r0 + row_block))
+                last = causal_last_key(rows, Nq, Nk) if causal else None
+                o, m, l = attention_rows_fp64(qf[b, h, rows], kf[b, hk], vf[b, hk], scale, last)
+                out[b, h, rows] = o
+                ms[b, h, rows] = m
+                ls[b, h, rows] = l
+    out = out.reshape(lead + (H, Nq, vf.shape[-1]))
+    ms = ms.reshape(lead + (H, Nq))
+    ls = ls.reshape(lead + (H, Nq))
+    if squeeze:
+        out, ms, ls = out[0], ms[0], ls[0]
     if return_stats:
-        return out, ms.reshape(lead + (Nq,)), ls.reshape(lead + (Nq,))
+        return out, ms, ls
     return out
 
 
@@ -275,7 +330,9 @@ def partial_state(s, V):
     if s.shape[1] == 0:
         return (np.full(s.shape[0], NEG_INF), np.zeros(s.shape[0]), np.zeros((s.shape[0], V.shape[1])))
     m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
+    live = np.isfinite(m)        # a row whose scores are all -inf (masked) keeps the identity state
+    p = np.zeros_like(s)
+    p[live] = np.exp(s[live] - m[live, None])
     return m, p.sum(axis=1), p @ V
 
 
@@ -338,9 +395,16 @@ def split_bounds(Nk: int, num_splits: int):
     return [((c * Nk) // num_splits, ((c + 1) * Nk) // num_splits) for c in range(num_splits)]
 
 
-def split_partial_states(q, k, v, scale, num_splits: int):
-    """Per-split (m, l, o) for one head: q [Nq, d], k, v [Nk, d] -> list of states over ``split_bounds``."""
+def split_partial_states(q, k, v, scale, num_splits: int, causal: bool = False):
+    """Per-split (m, l, o) for one head: q [Nq, d], k, v [Nk, d] -> list of states over ``split_bounds``.
+
+    With ``causal`` the scores of keys past ``causal_last_key`` are -inf first; a split
+    holding no key a row may see gives that row the identity state (-inf, 0, 0).
+    """
     s = scores_fp64(q, k, scale)
+    if causal:
+        last = causal_last_key(np.arange(s.shape[0]), s.shape[0], s.shape[1])
+        s = np.where(np.arange(s.shape[1])[None, :] <= last[:, None], s, NEG_INF)
     v = np.asarray(v, dtype=np.float64)
     return [partial_state(s[:, a:b], v[a:b]) for a, b in split_bounds(k.shape[0], num_splits)]
 

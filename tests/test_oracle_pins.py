@@ -333,3 +333,113 @@ def test_pages_oracle_magnitudes():
     p, V4, ref = _demo4()
     ebf = np.abs((oracle.round_to_bf16(p) @ V4) / p.sum() - ref).max() / np.abs(ref).max()
     assert _fig("pv_rel_err_bf16") / 10 ** 0.5 < ebf < _fig("pv_rel_err_bf16") * 10 ** 0.5
+
+
+# --- P10: the causal mask and grouped K/V heads ([FA-Simplified §7]) ----------------------------
+
+def _causal_brute(q, k, v, scale):
+    """Literal loops: query row i of Nq attends keys j = 0 .. i + (Nk - Nq), nothing else."""
+    Nq, Nk = len(q), len(k)
+    out = []
+    for i in range(Nq):
+        keys = range(0, i + (Nk - Nq) + 1)
+        s = [float(scale) * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j])) for j in keys]
+        mx = max(s)
+        p = [math.exp(x - mx) for x in s]
+        l = math.fsum(p)
+        out.append([math.fsum(p[n] * float(v[j][c]) for n, j in enumerate(keys)) / l for c in range(len(v[0]))])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("Nq,Nk,d", [(1, 1, 2), (5, 5, 3), (3, 7, 4), (1, 4, 2), (6, 6, 5), (4, 9, 3)])
+def test_causal_brute_force(Nq, Nk, d):
+    r = _rng(700 + Nq * 13 + Nk)
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    got = oracle.attention_fp64(q[None], k[None], v[None], 0.6, causal=True)[0]
+    assert np.max(np.abs(got - _causal_brute(q, k, v, 0.6))) < 1e-14
+
+
+def test_causal_square_matches_torch_sdpa():
+    """Nq = Nk: the usual decoder mask; torch's float64 attention with is_causal=True (its mask keeps j <= i)."""
+    r = _rng(710)
+    q, k, v = (r.standard_normal((2, 3, 37, 8)) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=0.3).numpy()
+    assert np.max(np.abs(oracle.attention_fp64(q, k, v, 0.3, causal=True) - ref)) < 1e-13
+
+
+def test_causal_rows_are_prefix_attention():
+    """Row i equals unmasked attention over the first i + Nk - Nq + 1 keys; the first row of a square problem
+    is v[0]; the last row of any problem is the unmasked result."""
+    r = _rng(711)
+    Nq, Nk, d = 19, 45, 6
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    got = oracle.attention_fp64(q[None], k[None], v[None], 0.4, causal=True)[0]
+    for i in range(Nq):
+        n = i + Nk - Nq + 1
+        ref = oracle.attention_fp64(q[None, i:i + 1], k[None, :n], v[None, :n], 0.4)[0, 0]
+        assert np.max(np.abs(got[i] - ref)) < 1e-14
+    full = oracle.attention_fp64(q[None], k[None], v[None], 0.4)[0]
+    assert np.max(np.abs(got[-1] - full[-1])) < 1e-14
+    sq = oracle.attention_fp64(q[None, :, :], k[None, :Nq], v[None, :Nq], 0.4, causal=True)[0]
+    assert np.max(np.abs(sq[0] - v[0])) == 0.0
+
+
+def test_causal_queries_are_the_last_positions():
+    """Nq < Nk: the result equals the last Nq rows of the square causal problem whose last queries are these
+    (the reading: the queries are the final positions of the key sequence)."""
+    r = _rng(712)
+    Nq, Nk, d = 7, 30, 5
+    qfull, k, v = r.standard_normal((Nk, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    square = oracle.attention_fp64(qfull[None], k[None], v[None], 0.5, causal=True)[0]
+    tail = oracle.attention_fp64(qfull[None, Nk - Nq:], k[None], v[None], 0.5, causal=True)[0]
+    assert np.max(np.abs(square[Nk - Nq:] - tail)) < 1e-14
+
+
+def test_causal_needs_nq_le_nk():
+    q = np.zeros((1, 5, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_fp64(q, q[:, :3], q[:, :3], 1.0, causal=True)
+
+
+def test_gqa_head_map():
+    """Consecutive query heads share a K/V head: H = 8 over H_kv = 2 reads 0,0,0,0,1,1,1,1; MQA reads head 0."""
+    assert [oracle.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head_of(h, 6, 1) for h in range(6)] == [0] * 6
+    assert [oracle.kv_head_of(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+@pytest.mark.parametrize("H,H_kv,causal", [(8, 2, False), (6, 1, False), (4, 4, False), (8, 2, True), (6, 3, True)])
+def test_gqa_matches_torch_sdpa(H, H_kv, causal):
+    """torch's float64 attention with enable_gqa=True (K/V heads repeated to the query heads, in order)."""
+    r = _rng(720 + H * 7 + H_kv)
+    q = r.standard_normal((2, H, 23, 8))
+    k, v = r.standard_normal((2, H_kv, 23, 8)), r.standard_normal((2, H_kv, 23, 8))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.35,
+        enable_gqa=True).numpy()
+    assert np.max(np.abs(oracle.attention_fp64(q, k, v, 0.35, causal=causal) - ref)) < 1e-13
+
+
+def test_gqa_equals_mha_on_repeated_heads():
+    r = _rng(730)
+    q = r.standard_normal((1, 6, 11, 4))
+    k, v = r.standard_normal((1, 2, 15, 4)), r.standard_normal((1, 2, 15, 4))
+    rep = oracle.attention_fp64(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.5, causal=True)
+    assert np.max(np.abs(oracle.attention_fp64(q, k, v, 0.5, causal=True) - rep)) == 0.0
+
+
+def test_causal_split_states_merge_to_causal_attention():
+    """Split states under the mask (some rows see none of a split's keys) merge, in any order, to the masked result."""
+    r = _rng(740)
+    Nq, Nk, d = 9, 40, 5
+    q, k, v = r.standard_normal((Nq, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    states = oracle.split_partial_states(q, k, v, 0.45, 8, causal=True)
+    m0 = states[-1][0]
+    assert np.sum(np.isneginf(m0)) > 0 and np.all(states[-1][1][np.isneginf(m0)] == 0)
+    ref = oracle.attention_fp64(q[None], k[None], v[None], 0.45, causal=True)[0]
+    for order in (None, list(range(7, -1, -1)), [3, 0, 6, 1, 7, 2, 5, 4]):
+        got = oracle.finish_state(oracle.merge_sequential(states, order))
+        assert np.max(np.abs(got - ref)) < 1e-14
