@@ -1,10 +1,12 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|long_seq|decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload headline|long_seq|causal|decode|gqa_decode] [--no-cpu]
 
-A step is one fa_fwd over the whole batch (headline, long_seq) or one fa_fwd_split + fa_merge_states
-pair (decode). Inputs are generated and resident in HBM before the timed region. Prints ONE JSON line.
-The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per step).
+A step is one forward over the whole batch (headline, long_seq, causal) or one split + merge pair
+(decode, gqa_decode). Inputs are generated and resident in HBM before the timed region. Prints ONE
+JSON line. The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per
+step); the causal workload counts 4*d flops per visible (query, key) pair.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="headline", choices=["headline", "long_seq", "decode"])
+    p.add_argument("--workload", default="headline", choices=["headline", "long_seq", "causal", "decode", "gqa_decode"])
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
@@ -98,9 +100,11 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "decode": si.DECODE_BF16}[args.workload]
+    wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16,
+          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16}[args.workload]
+    is_decode = args.workload in ("decode", "gqa_decode")
 
-    if args.workload == "decode":
+    if is_decode:
         q, k, v = si.decode_inputs_device(wl, dev)
     else:
         qh, kh, vh = si.workload_inputs(wl)
@@ -117,7 +121,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.workload == "decode":
+    if is_decode:
         S = wl.num_splits
         pm = torch.empty((S, wl.B, wl.H, wl.Nq), device=dev, dtype=torch.float32)
         pl = torch.empty_like(pm)
@@ -138,7 +142,7 @@ def main():
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            fa.fwd(q, k, v, scale=wl.scale, out=o)
+            fa.fwd(q, k, v, scale=wl.scale, out=o, causal=wl.causal)
             if ev is not None:
                 ev[1].record(stream)
 
@@ -169,28 +173,32 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) draws, see seeded_inputs)"}
-    if args.workload == "decode":
+    if is_decode:
         split_ms = avg_launch_ms
-        kv_bytes = 2.0 * wl.B * wl.H * wl.Nk * wl.d * 2
+        kv_bytes = 2.0 * wl.B * wl.kv_heads * wl.Nk * wl.d * 2
         alg_bytes = kv_bytes + wl.B * wl.H * wl.d * 2 + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4
         step_bytes = alg_bytes + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4 + wl.B * wl.H * wl.d * 4
         result.update({"metric": "split-KV decode HBM GB/s (K+V bytes / step time)", "unit": "GB/s",
                        "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
-                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "Nk": wl.Nk, "d": wl.d,
-                                  "num_splits": wl.num_splits, "merge_order": "default_rng(5).permutation(16)"}})
+                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "H_kv": wl.kv_heads, "Nq": wl.Nq,
+                                  "Nk": wl.Nk, "d": wl.d, "num_splits": wl.num_splits,
+                                  "merge_order": f"default_rng({wl.seed}).permutation({wl.num_splits})"}})
         achieved = alg_bytes / (split_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "kernel": "decode_kernel (split)", "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                              **launch_stats, "traffic": traffic_for("decode", source_hash("decode.hip"))}
+                              **launch_stats, "traffic": traffic_for(args.workload, source_hash("decode.hip"))}
         result["step_bytes"] = step_bytes
     else:
         flops = wl.flops
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         if args.workload == "long_seq":
             result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=16384,d=128 bf16, K x3; % of MFMA peak"
+        if args.workload == "causal":
+            result["metric"] = ("FA fwd causal TFLOP/s (4*d per visible query-key pair, B*H*N(N+1)/2 pairs) "
+                                "at N=4096,d=64 bf16; % of MFMA peak")
         result.update({"unit": "TFLOP/s", "value": tflops,
                        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
-                                  "causal": False, "out_dtype": "fp32"}})
+                                  "causal": wl.causal, "out_dtype": "fp32"}})
         achieved = flops / (avg_launch_ms * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "kernel": "fwd_mfma_kernel", "achieved": achieved,
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

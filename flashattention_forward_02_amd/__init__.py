@@ -5,6 +5,8 @@ call of the C ABI declared in include/fa.h; all arithmetic runs in the library's
 Outputs are allocated with torch on the inputs' device (the library itself never allocates).
 
     O = fwd(q, k, v)                                  # q [B,H,Nq,d], k/v [B,H,Nk,d]
+    O = fwd(q, k, v, causal=True)                     # row i sees keys j <= i + Nk - Nq
+    O = fwd(q, k_g, v_g)                              # grouped K/V heads: k_g, v_g [B,H_kv,Nk,d]
     part = fwd_split(q, k, v, num_splits=16)          # (m, l, o) partial states per key range
     O = merge_states(*part, order=[...])              # fold them in the given order
 """
@@ -49,17 +51,21 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be contiguous")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
-    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
-        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if (k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3] or k.shape[1] < 1
+            or q.shape[1] % k.shape[1]):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} "
+                         "(k and v: [B, H_kv, Nk, d] with H a multiple of H_kv)")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k and v must be on one device")
 
 
-def fwd(q, k, v, scale=None, out_dtype=None, return_stats=False, out=None):
-    """O = softmax(scale * q k^T) v per (b, h); scale defaults to 1/sqrt(d). See fa_fwd in include/fa.h.
+def fwd(q, k, v, scale=None, out_dtype=None, return_stats=False, out=None, causal=False):
+    """O = softmax(scale * q k^T) v per (b, h); scale defaults to 1/sqrt(d). See fa_fwd / fa_fwd_ext in include/fa.h.
 
+    k and v may have fewer heads than q (grouped K/V heads: query head h reads K/V head h // (H // H_kv)).
+    ``causal``: row i sees keys j <= i + Nk - Nq only (needs Nq <= Nk).
     With ``return_stats`` also returns m (row max of the scaled scores) and l (sum of exp(s - m)), fp32 [B,H,Nq].
     """
     torch = _torch()
@@ -77,15 +83,26 @@ def fwd(q, k, v, scale=None, out_dtype=None, return_stats=False, out=None):
     if return_stats:
         m = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
         l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _native.check(_native.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                 m.data_ptr() if m is not None else None, l.data_ptr() if l is not None else None,
-                                 B, H, Nq, Nk, d, float(scale), _dtype_code(q.dtype), _dtype_code(out_dtype),
-                                 _stream_ptr(q.device)))
+    mp = m.data_ptr() if m is not None else None
+    lp = l.data_ptr() if l is not None else None
+    H_kv = k.shape[1]
+    if H_kv == H and not causal:
+        _native.check(_native.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), mp, lp,
+                                     B, H, Nq, Nk, d, float(scale), _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                     _stream_ptr(q.device)))
+    else:
+        _native.check(_native.fa_fwd_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), mp, lp,
+                                         B, H, H_kv, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q.dtype),
+                                         _dtype_code(out_dtype), _stream_ptr(q.device)))
     return (out, m, l) if return_stats else out
 
 
-def fwd_split(q, k, v, num_splits, scale=None, workspace=None):
-    """Split-KV partial states (part_m [S,B,H,Nq], part_l, part_o [S,B,H,Nq,d], fp32). See fa_fwd_split."""
+def fwd_split(q, k, v, num_splits, scale=None, workspace=None, causal=False):
+    """Split-KV partial states (part_m [S,B,H,Nq], part_l, part_o [S,B,H,Nq,d], fp32). See fa_fwd_split(_ext).
+
+    Grouped K/V heads and ``causal`` as in ``fwd``; under the mask a key range a row cannot see gives it the
+    empty state (-inf, 0, 0).
+    """
     torch = _torch()
     _check_qkv(q, k, v)
     B, H, Nq, d = q.shape
@@ -98,9 +115,16 @@ def fwd_split(q, k, v, num_splits, scale=None, workspace=None):
         part_o = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
     else:
         part_m, part_l, part_o = workspace
-    _native.check(_native.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), part_m.data_ptr(),
-                                       part_l.data_ptr(), part_o.data_ptr(), num_splits, B, H, Nq, Nk, d,
-                                       float(scale), _dtype_code(q.dtype), _stream_ptr(q.device)))
+    H_kv = k.shape[1]
+    if H_kv == H and not causal:
+        _native.check(_native.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), part_m.data_ptr(),
+                                           part_l.data_ptr(), part_o.data_ptr(), num_splits, B, H, Nq, Nk, d,
+                                           float(scale), _dtype_code(q.dtype), _stream_ptr(q.device)))
+    else:
+        _native.check(_native.fa_fwd_split_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), part_m.data_ptr(),
+                                               part_l.data_ptr(), part_o.data_ptr(), num_splits, B, H, H_kv, Nq, Nk,
+                                               d, float(scale), int(bool(causal)), _dtype_code(q.dtype),
+                                               _stream_ptr(q.device)))
     return part_m, part_l, part_o
 
 

@@ -94,15 +94,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
   const int rest = blockIdx.x / S;
   const int row = rest % a.Nq;
   const size_t head = rest / a.Nq;
+  const size_t kvh = kv_head_index((int)(head / a.H), (int)(head % a.H), a.H, a.H_kv);
   const int kbeg = split_begin(split, a.Nk, S);
-  const int kend = split_begin(split + 1, a.Nk, S);
+  // Under the causal mask this row sees keys up to row + causal_off; the range may be empty.
+  const int kend = a.causal ? min(split_begin(split + 1, a.Nk, S), row + a.causal_off + 1)
+                            : split_begin(split + 1, a.Nk, S);
 
   const int tid = threadIdx.x;
   const int g = tid >> 4;
   const int t = tid & 15;
   const T* __restrict__ Qr = static_cast<const T*>(a.q) + (head * a.Nq + row) * (size_t)D + t * DL;
-  const T* __restrict__ K = static_cast<const T*>(a.k) + head * (size_t)a.Nk * D + t * DL;
-  const T* __restrict__ V = static_cast<const T*>(a.v) + head * (size_t)a.Nk * D + t * DL;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D + t * DL;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D + t * DL;
 
   float q[DL];
   load_row<T, DL>(Qr, q);
@@ -196,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
     else w[i] = __builtin_amdgcn_exp2f((mi - M) * c2);
     L = __builtin_fmaf(w[i], sh_l[i], L);
   }
-  const float m_nat = kAccurate ? M : a.scale * M;
+  // An empty range (possible only under the mask, in split mode) leaves M = -inf, L = 0, o = 0.
+  const float m_nat = (kAccurate || M == -INFINITY) ? M : a.scale * M;
   const size_t qrow = head * a.Nq + row;
   for (int c = tid; c < D; c += kThreads) {
     float o = 0.f;

@@ -64,7 +64,8 @@ float rescale_threshold() {
   return tau;
 }
 
-fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, float scale) {
+fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H, int H_kv, int Nq, int Nk,
+                      float scale, int causal) {
   fa::FwdArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -72,6 +73,9 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H,
   a.v = v;
   a.B = B;
   a.H = H;
+  a.H_kv = H_kv;
+  a.causal = causal;
+  a.causal_off = Nk - Nq;
   a.Nq = Nq;
   a.Nk = Nk;
   a.num_splits = 1;
@@ -86,28 +90,35 @@ fa_status launched(const char* fn, hipError_t e) {
   return FA_OK;
 }
 
-}  // namespace
+// Checks of the grouped-head count and the mask flag (fa_fwd_ext, fa_fwd_split_ext).
+fa_status check_ext(const char* fn, int H, int H_kv, int Nq, int Nk, int causal) {
+  if (H_kv < 1 || (H > 0 && H % H_kv != 0))
+    return fail(FA_EINVAL, "%s: H=%d must be a positive multiple of H_kv=%d", fn, H, H_kv);
+  if (causal != 0 && causal != 1) return fail(FA_EINVAL, "%s: causal=%d must be 0 or 1", fn, causal);
+  if (causal && Nq > Nk)
+    return fail(FA_EINVAL, "%s: the causal mask needs Nq <= Nk (Nq=%d, Nk=%d): rows would see no key", fn, Nq, Nk);
+  return FA_OK;
+}
 
-extern "C" {
-
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
-                 int Nq, int Nk, int d, float scale, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
-  g_last_error[0] = 0;
-  fa_status st = check_common("fa_fwd", q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out,
+                   int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype,
+                   fa_dtype out_dtype, void* stream) {
+  fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
   if (st != FA_OK) return st;
-  if (!o && (size_t)B * H * Nq != 0) return fail(FA_EINVAL, "fa_fwd: o must be a non-NULL device pointer");
+  if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
+  if (!o && (size_t)B * H * Nq != 0) return fail(FA_EINVAL, "%s: o must be a non-NULL device pointer", fn);
   if (out_dtype != FA_F32 && out_dtype != in_dtype)
-    return fail(FA_EINVAL, "fa_fwd: out_dtype=%d must be FA_F32 or equal to in_dtype=%d", (int)out_dtype, (int)in_dtype);
-  if (!aligned16(o)) return fail(FA_EINVAL, "fa_fwd: o must be 16-byte aligned");
-  if (!aligned4(m_out) || !aligned4(l_out)) return fail(FA_EINVAL, "fa_fwd: m_out and l_out must be 4-byte aligned");
+    return fail(FA_EINVAL, "%s: out_dtype=%d must be FA_F32 or equal to in_dtype=%d", fn, (int)out_dtype, (int)in_dtype);
+  if (!aligned16(o)) return fail(FA_EINVAL, "%s: o must be 16-byte aligned", fn);
+  if (!aligned4(m_out) || !aligned4(l_out)) return fail(FA_EINVAL, "%s: m_out and l_out must be 4-byte aligned", fn);
   if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
-  const size_t heads = (size_t)B * H;
-  const size_t obytes = heads * Nq * d * dtype_size(out_dtype);
-  const size_t qbytes = heads * Nq * d * dtype_size(in_dtype), kvbytes = heads * Nk * d * dtype_size(in_dtype);
+  const size_t obytes = (size_t)B * H * Nq * d * dtype_size(out_dtype);
+  const size_t qbytes = (size_t)B * H * Nq * d * dtype_size(in_dtype);
+  const size_t kvbytes = (size_t)B * H_kv * Nk * d * dtype_size(in_dtype);
   if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, kvbytes) || overlaps(o, obytes, v, kvbytes))
-    return fail(FA_EINVAL, "fa_fwd: o overlaps q, k or v");
+    return fail(FA_EINVAL, "%s: o overlaps q, k or v", fn);
 
-  fa::FwdArgs a = make_args(q, k, v, B, H, Nq, Nk, scale);
+  fa::FwdArgs a = make_args(q, k, v, B, H, H_kv, Nq, Nk, scale, causal);
   a.o = o;
   a.m_out = m_out;
   a.l_out = l_out;
@@ -117,24 +128,24 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* m_
   if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
-  return launched("fa_fwd", e);
+  return launched(fn, e);
 }
 
-fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,
-                       int num_splits, int B, int H, int Nq, int Nk, int d, float scale, fa_dtype in_dtype,
-                       void* stream) {
-  g_last_error[0] = 0;
-  fa_status st = check_common("fa_fwd_split", q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const void* v, float* part_m, float* part_l,
+                         float* part_o, int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+                         int causal, fa_dtype in_dtype, void* stream) {
+  fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
   if (st != FA_OK) return st;
+  if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
   if ((!part_m || !part_l || !part_o) && (size_t)B * H * Nq != 0)
-    return fail(FA_EINVAL, "fa_fwd_split: part_m, part_l and part_o must be non-NULL");
+    return fail(FA_EINVAL, "%s: part_m, part_l and part_o must be non-NULL", fn);
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS || num_splits > Nk)
-    return fail(FA_EINVAL, "fa_fwd_split: num_splits=%d must be in [1, min(Nk=%d, %d)]", num_splits, Nk, FA_MAX_SPLITS);
+    return fail(FA_EINVAL, "%s: num_splits=%d must be in [1, min(Nk=%d, %d)]", fn, num_splits, Nk, FA_MAX_SPLITS);
   if (!aligned16(part_o) || !aligned4(part_m) || !aligned4(part_l))
-    return fail(FA_EINVAL, "fa_fwd_split: part_o must be 16-byte and part_m, part_l 4-byte aligned");
+    return fail(FA_EINVAL, "%s: part_o must be 16-byte and part_m, part_l 4-byte aligned", fn);
   if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
 
-  fa::FwdArgs a = make_args(q, k, v, B, H, Nq, Nk, scale);
+  fa::FwdArgs a = make_args(q, k, v, B, H, H_kv, Nq, Nk, scale, causal);
   a.part_m = part_m;
   a.part_l = part_l;
   a.part_o = part_o;
@@ -145,7 +156,42 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_
   if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
-  return launched("fa_fwd_split", e);
+  return launched(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
+                 int Nq, int Nk, int d, float scale, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  return fwd_impl("fa_fwd", q, k, v, o, m_out, l_out, B, H, H > 0 ? H : 1, Nq, Nk, d, scale, 0, in_dtype, out_dtype,
+                  stream);
+}
+
+fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
+                     int H_kv, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype, fa_dtype out_dtype,
+                     void* stream) {
+  g_last_error[0] = 0;
+  return fwd_impl("fa_fwd_ext", q, k, v, o, m_out, l_out, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, out_dtype,
+                  stream);
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,
+                       int num_splits, int B, int H, int Nq, int Nk, int d, float scale, fa_dtype in_dtype,
+                       void* stream) {
+  g_last_error[0] = 0;
+  return fwd_split_impl("fa_fwd_split", q, k, v, part_m, part_l, part_o, num_splits, B, H, H > 0 ? H : 1, Nq, Nk, d,
+                        scale, 0, in_dtype, stream);
+}
+
+fa_status fa_fwd_split_ext(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,
+                           int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                           fa_dtype in_dtype, void* stream) {
+  g_last_error[0] = 0;
+  return fwd_split_impl("fa_fwd_split_ext", q, k, v, part_m, part_l, part_o, num_splits, B, H, H_kv, Nq, Nk, d, scale,
+                        causal, in_dtype, stream);
 }
 
 fa_status fa_merge_states(const float* part_m, const float* part_l, const float* part_o, const int* order,

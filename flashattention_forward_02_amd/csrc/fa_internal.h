@@ -22,6 +22,9 @@ struct FwdArgs {
   float* part_l;
   float* part_o;
   int B, H, Nq, Nk;
+  int H_kv;         // K/V heads; query head h reads K/V head h / (H / H_kv)
+  int causal;       // 1: query row i sees keys j <= i + causal_off only
+  int causal_off;   // Nk - Nq
   int num_splits;   // 1 in full mode
   int split_mode;   // 0: final output, 1: partial states
   int out_dtype;    // Dtype of o (full mode)
@@ -47,6 +50,11 @@ struct MergeArgs {
 // Key range [split_begin(c), split_begin(c + 1)) of part c of a split-KV partition.
 __host__ __device__ inline int split_begin(int c, int Nk, int S) {
   return (int)(((long long)c * (long long)Nk) / (long long)S);
+}
+
+// Offset of K/V head (b, h / (H / H_kv)) in units of heads.
+__host__ __device__ inline size_t kv_head_index(int b, int h, int H, int H_kv) {
+  return (size_t)b * H_kv + h / (H / H_kv);
 }
 
 // Workgroup remap so that consecutive logical tiles run on one XCD. The dispatcher hands

@@ -57,16 +57,24 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
   const int h = rest % a.H;
   const int b = rest / a.H;
   const size_t head = (size_t)b * a.H + h;
+  const size_t kvh = kv_head_index(b, h, a.H, a.H_kv);
   const float* __restrict__ Q = static_cast<const float*>(a.q) + head * (size_t)a.Nq * D;
-  const float* __restrict__ K = static_cast<const float*>(a.k) + head * (size_t)a.Nk * D;
-  const float* __restrict__ V = static_cast<const float*>(a.v) + head * (size_t)a.Nk * D;
+  const float* __restrict__ K = static_cast<const float*>(a.k) + kvh * (size_t)a.Nk * D;
+  const float* __restrict__ V = static_cast<const float*>(a.v) + kvh * (size_t)a.Nk * D;
   const int kbeg = split_begin(split, a.Nk, a.num_splits);
-  const int kend = split_begin(split + 1, a.Nk, a.num_splits);
+  int kend = split_begin(split + 1, a.Nk, a.num_splits);
 
   const int tid = threadIdx.x;
   const int row = qt * ROWS + tid / LPR;
   const int col0 = (tid % LPR) * 32;
   const bool live = row < a.Nq;
+  // Causal mask: this row sees keys < row_end; the workgroup stops after the last key any of
+  // its rows sees (key tiles wholly past it are skipped).
+  int row_end = kend;
+  if (a.causal) {
+    row_end = min(kend, row + a.causal_off + 1);
+    kend = min(kend, min(a.Nq, (qt + 1) * ROWS) - 1 + a.causal_off + 1);
+  }
 
   float q[32], acc[32], comp[32];
 #pragma unroll
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
       }
 #pragma unroll
       for (int off = 1; off < LPR; off <<= 1) dot += __shfl_xor(dot, off);
-      s[j] = (j < nvalid) ? a.scale * dot : -INFINITY;
+      s[j] = (key0 + j < row_end) ? a.scale * dot : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float mnew = fmaxf(m, mx);
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
     lcomp *= alpha;
 #pragma unroll
     for (int j = 0; j < kBCF; ++j) {
-      const float p = (j < nvalid) ? expf(s[j] - mnew) : 0.f;
+      const float p = (key0 + j < row_end) ? expf(s[j] - mnew) : 0.f;
       kahan_add(l, lcomp, p);
 #pragma unroll
       for (int c = 0; c < 32; c += 4) {

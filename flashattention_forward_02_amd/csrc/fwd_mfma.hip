@@ -338,7 +338,7 @@ __device__ __forceinline__ void softmax_block(const f32x16_t (&s)[2], float& mra
   } else {
     const float mx = max_block(s);
     mraw = fmaxf(mraw, mx);
-    const float mx2 = mx * c2;
+    const float mx2 = mx == -INFINITY ? -INFINITY : mx * c2;  // a wholly masked tile (scale may be 0)
     move_ref<D>(first || (mx2 > m2ref + tau), mx2, first, m2ref, lsum, acc);
     rs = exps_block<D, T, TAIL>(s, m2ref, c2, p);
   }
@@ -369,7 +369,7 @@ __device__ __forceinline__ void mfma_phase_order_d128() {
 #endif
 }
 
-template <int D, typename T, bool FAST>
+template <int D, typename T, bool FAST, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_qtiles) {
   typedef Cfg<D, T> C;
   typedef typename C::v8 v8;
@@ -385,21 +385,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
 
   // ---- work item: (query tile, split, h, b) ----
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = wg % n_qtiles;
+  // Under the causal mask later query tiles see more keys: hand them out first.
+  const int qt = CAUSAL ? n_qtiles - 1 - wg % n_qtiles : wg % n_qtiles;
   int rest = wg / n_qtiles;
   const int split = rest % a.num_splits;
   rest /= a.num_splits;
   const int h = rest % a.H;
   const int b = rest / a.H;
   const size_t head = (size_t)b * a.H + h;
+  const size_t kvh = kv_head_index(b, h, a.H, a.H_kv);
   const T* __restrict__ Q = static_cast<const T*>(a.q) + head * (size_t)a.Nq * D;
-  const T* __restrict__ K = static_cast<const T*>(a.k) + head * (size_t)a.Nk * D;
-  const T* __restrict__ V = static_cast<const T*>(a.v) + head * (size_t)a.Nk * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
   const int kbeg = split_begin(split, a.Nk, a.num_splits);
-  const int kend = split_begin(split + 1, a.Nk, a.num_splits);
+  int kend = split_begin(split + 1, a.Nk, a.num_splits);
+  // Causal mask: row i sees keys <= i + causal_off. The workgroup's key range ends after the
+  // last key its last row sees (key tiles wholly past it are skipped); in split mode the range
+  // can be empty, and the rows then keep the empty state.
+  if constexpr (CAUSAL) kend = min(kend, min(a.Nq, (qt + 1) * C::BR) + a.causal_off);
   const int nkeys = kend - kbeg;
-  const int T_ = (nkeys + kBC - 1) / kBC;         // key tiles (>= 1)
-  const int last_valid = nkeys - (T_ - 1) * kBC;  // keys in the last tile (1..64)
+  const int T_ = nkeys > 0 ? (nkeys + kBC - 1) / kBC : 0;  // key tiles
+  // Tiles [0, n_plain) hold only keys every row of the workgroup sees: no masking there.
+  int n_plain = (nkeys % kBC == 0) ? T_ : T_ - 1;
+  if constexpr (CAUSAL) n_plain = min(n_plain, max(0, (qt * C::BR + a.causal_off + 1 - kbeg) / kBC));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -483,18 +491,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
     if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  auto phase_valu_tail = [&](int t, bool first) {
+  // Masked tiles: keys past the range end (a ragged last tile) or past the row's last visible
+  // key (causal) get score -inf.
+  auto phase_valu_masked = [&](int t, bool first) {
     valu_prologue(t);
+    const int k0 = kbeg + t * kBC;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int nb = 0; nb < NB; ++nb) {
+      int lim = kend - k0;
+      if constexpr (CAUSAL) lim = min(lim, qrow0 + nb * 32 + l32 + a.causal_off + 1 - k0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key >= last_valid) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s[nb][kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= lim) s[nb][kb][r] = -INFINITY;
         }
-      }
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       softmax_block<D, T, FAST, true>(s[nb], st.mraw[nb], st.m2ref[nb], st.lsum[nb], pf[nb], acc[nb], first, c2, tau,
@@ -503,33 +516,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
     __syncthreads();
   };
 
-  // ---- prologue: K(0) (and, staged, V(0)) resident; group B then sits out one phase ----
-  if (group_a) {
-    load_tile2<D, T, true>(K, lds_k[0], kbeg, kend, gw, lane);
-    if constexpr (STAGE) load_tile2<D, T, false>(V, lds_v[0], kbeg, kend, gw, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (!group_a) __syncthreads();
+  if (T_ > 0) {
+    // ---- prologue: K(0) (and, staged, V(0)) resident; group B then sits out one phase ----
+    if (group_a) {
+      load_tile2<D, T, true>(K, lds_k[0], kbeg, kend, gw, lane);
+      if constexpr (STAGE) load_tile2<D, T, false>(V, lds_v[0], kbeg, kend, gw, lane);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!group_a) __syncthreads();
 
-  // First tile, full tiles, partial last tile, then the final PV; every tile is one MFMA phase
-  // and one VALU phase. Only the first and the last tile take the variants with the first-tile
-  // and masking logic, so the steady-state loop carries one softmax body.
-  const bool partial = last_valid < kBC;
-  phase_mfma(0, false, true);
-  if (T_ == 1 && partial) phase_valu_tail(0, true);
-  else phase_valu_full(0, true);
-  const int nfull = partial ? T_ - 1 : T_;
-  for (int t = 1; t < nfull; ++t) {
-    phase_mfma(t, true, true);
-    phase_valu_full(t, false);
+    // First tile, unmasked tiles, masked tiles, then the final PV; every tile is one MFMA
+    // phase and one VALU phase. Only the first tile takes the first-tile logic, and the
+    // steady-state loop carries the unmasked softmax body. Without the causal mask at most
+    // the last tile is masked, and it is peeled out of the loop.
+    phase_mfma(0, false, true);
+    if (n_plain >= 1) phase_valu_full(0, true);
+    else phase_valu_masked(0, true);
+    for (int t = 1; t < n_plain; ++t) {
+      phase_mfma(t, true, true);
+      phase_valu_full(t, false);
+    }
+    if constexpr (CAUSAL) {
+      for (int t = n_plain > 1 ? n_plain : 1; t < T_; ++t) {
+        phase_mfma(t, true, true);
+        phase_valu_masked(t, false);
+      }
+    } else if (n_plain < T_ && T_ > 1) {
+      phase_mfma(T_ - 1, true, true);
+      phase_valu_masked(T_ - 1, false);
+    }
+    phase_mfma(T_, true, false);
+    if (group_a) __syncthreads();
   }
-  if (partial && T_ > 1) {
-    phase_mfma(T_ - 1, true, true);
-    phase_valu_tail(T_ - 1, false);
-  }
-  phase_mfma(T_, true, false);
-  if (group_a) __syncthreads();
 
   // ---- epilogue: re-express l (and o) relative to the true maximum; O = acc / l ----
 #pragma unroll
@@ -555,7 +574,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
         }
       }
     } else if constexpr (!FAST) {
-      const float to_true = __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
+      // A row that saw no key of this range (causal mask) keeps the empty state (-inf, 0, 0).
+      const bool empty = st.mraw[nb] == -INFINITY;
+      const float to_true = empty ? 0.f : __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
       const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -566,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
                  acc[nb][db][4 * g4 + 2] * to_true, acc[nb][db][4 * g4 + 3] * to_true);
         }
       if (hf == 0) {
-        a.part_m[prow] = a.scale * st.mraw[nb];
+        a.part_m[prow] = empty ? -INFINITY : a.scale * st.mraw[nb];
         a.part_l[prow] = st.lsum[nb] * to_true;
       }
     }
@@ -585,8 +606,11 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   // Full-output calls without row statistics take the sum-checked softmax; statistics, split
   // states and a zero threshold (the literal recurrence) take the running-max form.
   const bool fast = a.split_mode == 0 && !a.m_out && !a.l_out && a.rescale_threshold >= 1.f;
-  const void* k = fast ? reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, true>)
-                       : reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, false>);
+  const void* k;
+  if (a.causal) k = fast ? reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, true, true>)
+                         : reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, false, true>);
+  else k = fast ? reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, true, false>)
+                : reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, false, false>);
   return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 #define FA_MAX_SPLITS 256
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
@@ -86,6 +86,43 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v,
                        float* part_m, float* part_l, float* part_o,
                        int num_splits, int B, int H, int Nq, int Nk, int d, float scale,
                        fa_dtype in_dtype, void* stream);
+
+/*
+ * fa_fwd_ext -- fa_fwd with grouped K/V heads and an optional causal mask.
+ *
+ * "FlashAttention 简化版：Tiling + Online Softmax" §7 names both as the next steps after the
+ * plain forward pass (a causal mask folded into the tiling, for decoder models; multi-query /
+ * grouped-query attention, to cut K/V memory) without fixing a convention; these are the ones
+ * taken:
+ *   H_kv      number of K/V heads: k, v are [B,H_kv,Nk,d]; H must be a multiple of H_kv.
+ *             Query head h reads K/V head h / (H / H_kv) (consecutive query heads share one).
+ *             H_kv = H is fa_fwd; H_kv = 1 is multi-query attention.
+ *   causal    0: no mask. 1: query row i sees only keys j <= i + (Nk - Nq) -- the usual
+ *             decoder mask when Nq = Nk; with Nq < Nk the queries are the last Nq positions of
+ *             the key sequence (the last row sees every key). Requires Nq <= Nk, so every row
+ *             keeps at least one key. Masked scores are -inf: they take part in neither m, l
+ *             nor O.
+ * Everything else (q, o, m_out, l_out, scale, dtypes, errors) is as in fa_fwd. Key tiles that
+ * lie wholly past a query tile's last visible key are skipped, so a causal call does about
+ * half the work of an unmasked one at Nq = Nk.
+ */
+fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o,
+                     float* m_out, float* l_out,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                     fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_split_ext -- fa_fwd_split with grouped K/V heads and an optional causal mask.
+ *
+ * H_kv and causal as in fa_fwd_ext; the partition and the state layouts as in fa_fwd_split.
+ * Under the mask a part that holds no key a row may see gives that row the empty state
+ * m = -inf, l = 0, o = 0, which fa_merge_states weighs 0. (With Nq <= Nk part 0 always holds
+ * key 0, which every row sees.)
+ */
+fa_status fa_fwd_split_ext(const void* q, const void* k, const void* v,
+                           float* part_m, float* part_l, float* part_o,
+                           int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+                           int causal, fa_dtype in_dtype, void* stream);
 
 /*
  * fa_merge_states -- fold partial states into the attention output.

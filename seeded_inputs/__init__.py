@@ -147,15 +147,29 @@ class Workload:
     k_mult: float = 1.0
     num_splits: int = 0
     extra: dict = field(default_factory=dict)
+    H_kv: int = 0            # K/V heads (0: same as H)
+    causal: bool = False     # row i sees keys j <= i + Nk - Nq
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
         return fp32_inverse_sqrt(self.d)
 
     @property
+    def visible_pairs(self) -> float:
+        """(query, key) pairs that enter the softmax: Nq * Nk, or under the causal mask
+        sum_i (i + Nk - Nq + 1) = Nq (Nk - Nq + 1) + Nq (Nq - 1) / 2."""
+        if not self.causal:
+            return float(self.Nq) * self.Nk
+        return float(self.Nq) * (self.Nk - self.Nq + 1) + self.Nq * (self.Nq - 1) / 2.0
+
+    @property
     def flops(self) -> float:
-        """4*B*H*Nq*Nk*d: the two matrix products QK^T and PV."""
-        return 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        """4*d flops (the two matrix products QK^T and PV) per visible (query, key) pair, per (b, h)."""
+        return 4.0 * self.B * self.H * self.d * self.visible_pairs
 
 
 SINGLE_HEAD_FP32 = Workload("single_head_fp32 B=1 H=1 N=256 d=64", 1, 1, 256, 256, 64, "f32", 42)
@@ -165,6 +179,9 @@ BATCHED_QUERIES_LONG_KEYS = Workload("batched_queries Nq=4096 Nk=4096 d=64", 1, 
 HEADLINE_BF16 = Workload("headline B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096, 64, "bf16", 3)
 LONG_SEQ_BF16 = Workload("long_seq B=1 H=32 N=16384 d=128 bf16 Kx3", 1, 32, 16384, 16384, 128, "bf16", 4,
                          k_mult=3.0)
+CAUSAL_BF16 = Workload("causal B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096, 64, "bf16", 3, causal=True)
+GQA_DECODE_BF16 = Workload("gqa_decode B=16 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 6,
+                           num_splits=16, H_kv=8)
 DECODE_BF16 = Workload("split_kv_decode B=16 H=32 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 5,
                        num_splits=16)
 
@@ -202,8 +219,8 @@ def one_query_long_keys(seed: int = 0, S: int = 4096, d: int = 64, batched: bool
 def workload_inputs(w: Workload):
     """Host Q, K, V for a per-head-drawn workload (headline, long sequence, or any ad-hoc shape)."""
     q = per_head_tensor(w.seed, w.B, w.H, w.Nq, w.d, 0, w.dtype)
-    k = per_head_tensor(w.seed, w.B, w.H, w.Nk, w.d, 1, w.dtype, w.k_mult)
-    v = per_head_tensor(w.seed, w.B, w.H, w.Nk, w.d, 2, w.dtype)
+    k = per_head_tensor(w.seed, w.B, w.kv_heads, w.Nk, w.d, 1, w.dtype, w.k_mult)
+    v = per_head_tensor(w.seed, w.B, w.kv_heads, w.Nk, w.d, 2, w.dtype)
     return q, k, v
 
 
@@ -229,10 +246,11 @@ def device_draw(shape, seed: int, dtype: str, device, mult: float = 1.0):
 
 
 def decode_inputs_device(w: Workload, device):
-    """Q [B,H,1,d], K, V [B,H,Nk,d] for the split-KV decode workload, drawn on the device (seeds seed, seed+1, seed+2)."""
+    """Q [B,H,Nq,d], K, V [B,H_kv,Nk,d] for a split-KV decode workload, drawn on the device
+    (seeds 1000*seed + 0, 1, 2)."""
     q = device_draw((w.B, w.H, w.Nq, w.d), w.seed * 1000 + 0, w.dtype, device)
-    k = device_draw((w.B, w.H, w.Nk, w.d), w.seed * 1000 + 1, w.dtype, device, w.k_mult)
-    v = device_draw((w.B, w.H, w.Nk, w.d), w.seed * 1000 + 2, w.dtype, device)
+    k = device_draw((w.B, w.kv_heads, w.Nk, w.d), w.seed * 1000 + 1, w.dtype, device, w.k_mult)
+    v = device_draw((w.B, w.kv_heads, w.Nk, w.d), w.seed * 1000 + 2, w.dtype, device)
     return q, k, v
 
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert n.fa_abi_version() == 1
+    assert n.fa_abi_version() == 2
     assert [n.fa_status_string(s) for s in range(4)] == ["FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
     assert n.fa_status_string(99) == "FA_UNKNOWN_STATUS"
 
@@ -79,6 +79,52 @@ def test_fa_fwd_empty_work_is_ok_without_device():
     assert fwd(Nq=0, q=None, o=None) == n.FA_OK
     assert fwd(B=0, q=None, k=None, v=None, o=None) == n.FA_OK
     assert fwd(Nq=0, k=None) == n.FA_EINVAL      # K still holds B*H*Nk elements
+
+
+def fwd_ext(**kw):
+    a = dict(q=P, k=P, v=P, o=P * 2, m_out=None, l_out=None, B=1, H=8, H_kv=2, Nq=8, Nk=8, d=64, scale=0.125,
+             causal=1, in_dtype=n.FA_BF16, out_dtype=n.FA_F32, stream=None)
+    a.update(kw)
+    return n.fa_fwd_ext(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H_kv=0), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(H_kv=3), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(H_kv=16), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(causal=2), n.FA_EINVAL, "causal=2"),
+    (dict(causal=-1), n.FA_EINVAL, "causal=-1"),
+    (dict(Nq=9), n.FA_EINVAL, "Nq <= Nk"),
+    (dict(Nk=0), n.FA_EINVAL, "empty key set"),
+    (dict(d=96), n.FA_EUNSUPPORTED, "d=96"),
+    (dict(q=None), n.FA_EINVAL, "non-NULL"),
+    (dict(o=P), n.FA_EINVAL, "overlaps"),
+])
+def test_fa_fwd_ext_rejects(kw, status, msg):
+    assert fwd_ext(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_fa_fwd_ext_empty_work_is_ok_without_device():
+    assert fwd_ext(Nq=0) == n.FA_OK
+    assert fwd_ext(B=0, q=None, k=None, v=None, o=None) == n.FA_OK
+    assert fwd_ext(causal=0, Nq=0, Nk=3) == n.FA_OK      # the Nq <= Nk rule applies to causal calls only
+    assert fwd_ext(causal=1, Nq=0, Nk=3) == n.FA_OK
+    assert n.fa_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H_kv=3), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(causal=5), n.FA_EINVAL, "causal=5"),
+    (dict(Nq=65), n.FA_EINVAL, "Nq <= Nk"),
+    (dict(num_splits=65), n.FA_EINVAL, "num_splits"),
+])
+def test_fa_fwd_split_ext_rejects(kw, status, msg):
+    a = dict(q=P, k=P, v=P, part_m=P * 2, part_l=P * 3, part_o=P * 4, num_splits=4, B=1, H=4, H_kv=2, Nq=1, Nk=64,
+             d=128, scale=0.1, causal=1, in_dtype=n.FA_BF16, stream=None)
+    a.update(kw)
+    assert n.fa_fwd_split_ext(**a) == status
+    assert msg in n.fa_last_error()
 
 
 def split(**kw):
