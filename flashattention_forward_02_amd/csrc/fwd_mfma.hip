@@ -33,7 +33,7 @@
 //    stalls on them). At d = 64 they start in A's MFMA phase and A's VALU phase re-lays the raw
 //    V tile in LDS as ready-made PV operand fragments, so the MFMA phase reads V^T with plain
 //    16-byte reads instead of transposing ones. Both tiles are XOR-swizzled in 16-byte chunks
-//    (K: chunk ^ row % 8, V: chunk ^ 2 * (row % 4), picked by timing on gfx950) so the operand
+//    (K: chunk ^ (row / 2) % 8, V: chunk ^ 2 * (row % 4)) so the operand
 //    reads spread over the LDS banks. The swizzle is applied on the global side: the lane that
 //    fills LDS chunk (row, c) fetches global chunk (row, c ^ f(row)).
 //  * Scores are handled in base 2: with c = scale * log2(e), exp(s - m) = 2^(raw*c - m*c),
@@ -55,6 +55,8 @@
 //    from LDS), 32 at d = 128 (the accumulator doubles); 512 or 256 rows per workgroup.
 
 #include "fa_internal.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -143,10 +145,13 @@ struct RowState {
 };
 
 // XOR swizzles of the 16-byte chunks of LDS row r: chunk c of a K row is stored at c ^ swzk(r),
-// of a V row at c ^ swzv(r). Picked by timing the kernel under several swizzles on gfx950: the
-// K tile is read one row per lane, 16 bytes at a time; the V tile by transposing reads of
-// 4 rows x 8 bytes per 16-lane group.
-__device__ __forceinline__ int swzk(int r) { return (r & 7); }
+// of a V row at c ^ swzv(r). The K tile is read one row per lane, 16 bytes at a time. With 64
+// four-byte banks (256 bytes per cycle, measured ~246 B/clk per CU), 16 lanes of a 16-byte read
+// go in one cycle when they hit 16 different 16-byte bank groups; a 128-byte K row spans half of
+// them, so rows r and r + 1 alternate halves and (r >> 1) & 7 spreads 16 consecutive rows over
+// all 16 groups (r & 7 repeats after 8 rows: a two-way conflict). The V tile is read by
+// transposing reads of 4 rows x 8 bytes per 16-lane group; its swizzle was picked by timing.
+__device__ __forceinline__ int swzk(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swzv(int r) { return ((r & 3) << 1); }
 
 // HBM -> LDS of one 64-row K or V tile, one quarter per group-A wave (gw = 0..3). Rows past
@@ -274,17 +279,20 @@ __device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typ
 //   FAST = true:  no running max; reference moves when the tile's row sum leaves [0, 2^tau].
 template <int D, typename T, bool TAIL>
 __device__ __forceinline__ float exps_block(const f32x16_t (&s)[2], float ref, float c2, float (&p)[32]) {
-  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) p[i] = __builtin_fmaf(s[i >> 4][i & 15], c2, -ref);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 4][i & 15], c2, -ref));
+    float x = __builtin_amdgcn_exp2f(p[i]);
     if constexpr (TAIL) {
       if (s[i >> 4][i & 15] == -INFINITY) x = 0.f;
     }
     p[i] = x;
-    rs += x;
   }
-  return xhalf_sum(rs);
+  float r4[4] = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+  for (int i = 4; i < 32; ++i) r4[i & 3] += p[i];
+  return xhalf_sum((r4[0] + r4[1]) + (r4[2] + r4[3]));
 }
 
 __device__ __forceinline__ float max_block(const f32x16_t (&s)[2]) {
@@ -369,6 +377,78 @@ __device__ __forceinline__ void mfma_phase_order_d128() {
 #endif
 }
 
+// The d = 64 MFMA phase (PV of the previous tile from staged V fragments, then S of this tile) as
+// a fixed instruction sequence: 8 groups of 2 LDS reads + 4 MFMAs, the reads of each group issued
+// between the MFMAs of the group before. A probe of one wave issuing 32x32x16 MFMAs with LDS
+// operands measured 43.5 cycles per MFMA in the compiler's order (two reads, wait for both,
+// four MFMAs: nothing in flight during the wait) and 35.6 in this one (32 is the matrix-core
+// rate). Reads, waits and MFMAs are inline asm so that the order is kept. Each wait takes the
+// registers it guards as in-out operands, so no MFMA that reads them can be placed before it.
+// The compiler does not see the MFMA latency inside asm, so the sequence ends with the wait
+// states a VALU read of an MFMA result needs.
+#define FA_RD(dst, addr, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(dst) : "v"(addr))
+#define FA_WAIT0(x, y) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y))
+#define FA_MF_BF16(acc, a, b) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+#define FA_MF0_BF16(acc, a, b) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b))
+#define FA_MF_F16(acc, a, b) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+#define FA_MF0_F16(acc, a, b) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b))
+
+template <typename T>
+__device__ __forceinline__ void mfma_acc(f32x16_t& acc, const typename Mma<T>::v8& a, const typename Mma<T>::v8& b) {
+  if constexpr (std::is_same<T, __bf16>::value) FA_MF_BF16(acc, a, b); else FA_MF_F16(acc, a, b);
+}
+template <typename T>
+__device__ __forceinline__ void mfma_zero(f32x16_t& acc, const typename Mma<T>::v8& a, const typename Mma<T>::v8& b) {
+  if constexpr (std::is_same<T, __bf16>::value) FA_MF0_BF16(acc, a, b); else FA_MF0_F16(acc, a, b);
+}
+
+// vaddr: LDS byte address of this lane's first staged V fragment (buffer + lane * 16);
+// kaddr[ks]: LDS byte address of this lane's K chunk of k-step ks in key block 0 (block 1 is +4096).
+template <typename T>
+__device__ __forceinline__ void mfma_phase_d64(unsigned vaddr, const unsigned (&kaddr)[4],
+                                               const typename Mma<T>::v8 (&pf)[2][4], const typename Mma<T>::v8 (&qf)[2][4],
+                                               f32x16_t (&acc)[2][2], f32x16_t (&s)[2][2]) {
+  typedef typename Mma<T>::v8 v8;
+  v8 r0a, r0b, r1a, r1b;
+  // PV: group g = fragments (g, db 0) and (g, db 1) at (2g + db) * 1024
+  FA_RD(r0a, vaddr, 0); FA_RD(r0b, vaddr, 1024);
+  FA_WAIT0(r0a, r0b);
+  mfma_acc<T>(acc[0][0], r0a, pf[0][0]); FA_RD(r1a, vaddr, 2048);
+  mfma_acc<T>(acc[1][0], r0a, pf[1][0]); mfma_acc<T>(acc[0][1], r0b, pf[0][0]); FA_RD(r1b, vaddr, 3072);
+  mfma_acc<T>(acc[1][1], r0b, pf[1][0]);
+  FA_WAIT0(r1a, r1b);
+  mfma_acc<T>(acc[0][0], r1a, pf[0][1]); FA_RD(r0a, vaddr, 4096);
+  mfma_acc<T>(acc[1][0], r1a, pf[1][1]); mfma_acc<T>(acc[0][1], r1b, pf[0][1]); FA_RD(r0b, vaddr, 5120);
+  mfma_acc<T>(acc[1][1], r1b, pf[1][1]);
+  FA_WAIT0(r0a, r0b);
+  mfma_acc<T>(acc[0][0], r0a, pf[0][2]); FA_RD(r1a, vaddr, 6144);
+  mfma_acc<T>(acc[1][0], r0a, pf[1][2]); mfma_acc<T>(acc[0][1], r0b, pf[0][2]); FA_RD(r1b, vaddr, 7168);
+  mfma_acc<T>(acc[1][1], r0b, pf[1][2]);
+  FA_WAIT0(r1a, r1b);
+  mfma_acc<T>(acc[0][0], r1a, pf[0][3]); FA_RD(r0a, kaddr[0], 0);
+  mfma_acc<T>(acc[1][0], r1a, pf[1][3]); mfma_acc<T>(acc[0][1], r1b, pf[0][3]); FA_RD(r0b, kaddr[0], 4096);
+  mfma_acc<T>(acc[1][1], r1b, pf[1][3]);
+  // S: group ks = K chunks of key blocks 0 and 1
+  FA_WAIT0(r0a, r0b);
+  mfma_zero<T>(s[0][0], r0a, qf[0][0]); FA_RD(r1a, kaddr[1], 0);
+  mfma_zero<T>(s[1][0], r0a, qf[1][0]); mfma_zero<T>(s[0][1], r0b, qf[0][0]); FA_RD(r1b, kaddr[1], 4096);
+  mfma_zero<T>(s[1][1], r0b, qf[1][0]);
+  FA_WAIT0(r1a, r1b);
+  mfma_acc<T>(s[0][0], r1a, qf[0][1]); FA_RD(r0a, kaddr[2], 0);
+  mfma_acc<T>(s[1][0], r1a, qf[1][1]); mfma_acc<T>(s[0][1], r1b, qf[0][1]); FA_RD(r0b, kaddr[2], 4096);
+  mfma_acc<T>(s[1][1], r1b, qf[1][1]);
+  FA_WAIT0(r0a, r0b);
+  mfma_acc<T>(s[0][0], r0a, qf[0][2]); FA_RD(r1a, kaddr[3], 0);
+  mfma_acc<T>(s[1][0], r0a, qf[1][2]); mfma_acc<T>(s[0][1], r0b, qf[0][2]); FA_RD(r1b, kaddr[3], 4096);
+  mfma_acc<T>(s[1][1], r0b, qf[1][2]);
+  FA_WAIT0(r1a, r1b);
+  mfma_acc<T>(s[0][0], r1a, qf[0][3]);
+  mfma_acc<T>(s[1][0], r1a, qf[1][3]); mfma_acc<T>(s[0][1], r1b, qf[0][3]);
+  mfma_acc<T>(s[1][1], r1b, qf[1][3]);
+  // an MFMA result read by the VALU needs 18 wait states after the MFMA (16-pass worst case)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+}
+
 template <int D, typename T, bool FAST, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_qtiles) {
   typedef Cfg<D, T> C;
@@ -431,6 +511,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
     }
   }
 
+  // d = 64: LDS byte addresses of this lane's MFMA-phase reads (per buffer)
+  // (buffer 0; buffer 1 is ELEMS elements further)
+  unsigned vaddr0 = 0u, kaddr0[4] = {0u, 0u, 0u, 0u};
+  if constexpr (D == 64) {
+    vaddr0 = (unsigned)(__UINTPTR_TYPE__)(lds_void_t*)&lds_vf[0][lane * 8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r = l32, ch = ks * 2 + hf;
+      kaddr0[ks] = (unsigned)(__UINTPTR_TYPE__)(lds_void_t*)&lds_k[0][r * D + ((ch ^ swzk(r)) << 3)];
+    }
+  }
   const float c2 = a.scale_log2e;
   const float tau = a.rescale_threshold;
   const float bound = __builtin_amdgcn_exp2f(tau);
@@ -462,11 +553,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
         load_tile2<D, T, true>(K, lds_k[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane);
         load_tile2<D, T, false>(V, lds_v[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane);
       }
-      if (do_pv) pv_staged<D, T>(lds_vf[(t - 1) & 1], pf, acc, lane);
+      if (do_pv && do_s) {
+        const unsigned vo = ((t - 1) & 1) * (unsigned)(C::ELEMS * sizeof(T));
+        const unsigned ko = (t & 1) * (unsigned)(C::ELEMS * sizeof(T));
+        const unsigned kaddr[4] = {kaddr0[0] + ko, kaddr0[1] + ko, kaddr0[2] + ko, kaddr0[3] + ko};
+        mfma_phase_d64<T>(vaddr0 + vo, kaddr, pf, qf, acc, s);
+      } else if (do_pv) {
+        pv_staged<D, T>(lds_vf[(t - 1) & 1], pf, acc, lane);
+      }
     } else {
       if (do_pv) pv_tile<D, T>(lds_v[(t - 1) & 1], pf, acc, lane);
     }
-    if (do_s) s_tile<D, T>(lds_k[t & 1], qf, s, lane);
+    if (do_s && !(STAGE && do_pv)) s_tile<D, T>(lds_k[t & 1], qf, s, lane);
     if constexpr (D == 128) {
       if (do_pv && do_s) mfma_phase_order_d128<2, 0>();
     }
