@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the FlashAttention forward pass.
+"""fp64 CPU oracle for the FlashAttention forward pass and its gradients.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run anything in this package.
@@ -35,6 +35,12 @@ What each function is pinned against (tests/test_oracle_pins.py):
   rows of the square problem; masked split states merge to the masked result.
 * grouped K/V heads (``kv_head_of``, K/V with fewer heads than Q) -- the head map
   written out; torch's float64 attention with enable_gqa; MHA on repeated K/V heads.
+* ``attention_backward_fp64`` (dq, dk, dv, log-sum-exp, D) -- central finite differences
+  of the forward definition; torch's float64 autograd through its own softmax (causal
+  and grouped heads included); closed forms (one key, zero scale, constant V); the
+  shift invariance sum_j dK_j = 0; D_i = sum_c dO_ic O_ic; the log-sum-exp against
+  scipy's; [FA-Fill Exercise 5]'s blocked recomputation of dV from the stored (m, l),
+  on the exercise's own recipe (torch seed 42, N = 64, d = 32, blocks of 16).
 
 Parity unpinned: nothing in this package. (The exact bf16 error of a GPU kernel
 depends on where its tiles fall and is bounded by the tolerance, not pinned.)
@@ -62,4 +68,9 @@ from .attention import (  # noqa: F401
     brute_force_attention,
     round_to_bf16,
     round_to_f16,
+)
+from .backward import (  # noqa: F401
+    attention_backward_fp64,
+    attention_loss_fp64,
+    dv_from_statistics_blocked,
 )
