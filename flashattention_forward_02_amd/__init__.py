@@ -1,4 +1,4 @@
-"""FlashAttention forward for AMD MI355X (gfx950): Python face of libfa.so.
+"""FlashAttention forward (and its gradients) for AMD MI355X (gfx950): Python face of libfa.so.
 
 Every function here marshals torch tensors (device memory, the current HIP stream) into a
 call of the C ABI declared in include/fa.h; all arithmetic runs in the library's HIP kernels.
@@ -9,6 +9,8 @@ Outputs are allocated with torch on the inputs' device (the library itself never
     O = fwd(q, k_g, v_g)                              # grouped K/V heads: k_g, v_g [B,H_kv,Nk,d]
     part = fwd_split(q, k, v, num_splits=16)          # (m, l, o) partial states per key range
     O = merge_states(*part, order=[...])              # fold them in the given order
+    O, lse = fwd_lse(q, k, v)                         # plus each row's log-sum-exp
+    dq, dk, dv = bwd(q, k, v, O, dO, lse)             # gradients, P recomputed from lse
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ import math
 from . import _native
 from ._native import FaError, FA_F32, FA_BF16, FA_F16  # noqa: F401
 
-__all__ = ["fwd", "fwd_split", "merge_states", "FaError", "lib_path"]
+__all__ = ["fwd", "fwd_lse", "bwd", "fwd_split", "merge_states", "FaError", "lib_path"]
 
 lib_path = _native.LIB_PATH
 
@@ -149,3 +151,54 @@ def merge_states(part_m, part_l, part_o, order=None, out_dtype=None, return_stat
                                           _dtype_code(out_dtype), m.data_ptr() if m is not None else None,
                                           l.data_ptr() if l is not None else None, _stream_ptr(part_o.device)))
     return (out, m, l) if return_stats else out
+
+
+def fwd_lse(q, k, v, scale=None, out_dtype=None, causal=False, out=None):
+    """(O, lse): fwd plus each row's log-sum-exp m + ln(l) of the scaled scores, fp32 [B,H,Nq]. See fa_fwd_lse."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, H, Nq, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of out_dtype")
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _native.check(_native.fa_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     B, H, k.shape[1], Nq, Nk, d, float(scale), int(bool(causal)),
+                                     _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)))
+    return out, lse
+
+
+def bwd(q, k, v, o, dout, lse, scale=None, causal=False, return_delta=False):
+    """(dq, dk, dv), fp32, of O = softmax(scale q k^T) v given dL/dO. See fa_bwd.
+
+    ``o`` and ``lse`` come from ``fwd_lse`` on the same inputs; ``dout`` has q's dtype (bf16 or fp16).
+    dk and dv have k's shape (with grouped K/V heads they sum over the query heads of a group).
+    With ``return_delta`` also returns D = rowsum(dout * o), fp32 [B,H,Nq].
+    """
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t, dt in (("o", o, None), ("dout", dout, q.dtype)):
+        if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous [B, H, Nq, d] tensor on q's device")
+        if dt is not None and t.dtype != dt:
+            raise TypeError(f"{name} must have q's dtype")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _native.check(_native.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 B, H, k.shape[1], Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q.dtype),
+                                 _dtype_code(o.dtype), _stream_ptr(q.device)))
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)

@@ -13,8 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 256
-EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_merge_states", "fa_status_string",
-           "fa_last_error", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_fwd_lse", "fa_bwd", "fa_merge_states",
+           "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -35,6 +35,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_ext.restype = I
         L.fa_fwd_split_ext.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
         L.fa_fwd_split_ext.restype = I
+        L.fa_fwd_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+        L.fa_fwd_lse.restype = I
+        L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+        L.fa_bwd.restype = I
         L.fa_merge_states.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, P, P]
         L.fa_merge_states.restype = I
         L.fa_status_string.argtypes = [I]
@@ -74,6 +78,16 @@ def fa_fwd_split_ext(q, k, v, part_m, part_l, part_o, num_splits, B, H, H_kv, Nq
                      stream):
     return lib().fa_fwd_split_ext(q, k, v, part_m, part_l, part_o, num_splits, B, H, H_kv, Nq, Nk, d, scale, causal,
                                   in_dtype, stream)
+
+
+def fa_fwd_lse(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, out_dtype, stream):
+    return lib().fa_fwd_lse(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, out_dtype, stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, o_dtype,
+           stream):
+    return lib().fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype,
+                        o_dtype, stream)
 
 
 def fa_merge_states(part_m, part_l, part_o, order, num_splits, B, H, Nq, d, o, out_dtype, m_out, l_out, stream):

@@ -1,0 +1,442 @@
+// FlashAttention backward pass for bf16 / fp16 inputs on the gfx950 matrix cores.
+//
+// What is computed. "Flash Attention 代码填空 (Level 2-3)", Exercise 5: the backward pass keeps
+// no score matrix; it recomputes P block by block from the forward pass's row statistics and
+// accumulates dV_j = sum_i P_ij^T dO_i. "CS349E 第 11 讲 01_online_softmax.py" notes that only the
+// log-sum-exp L = m + ln(l) of each row needs to be kept, so P_ij = exp(S_ij - L_i). dQ and dK
+// follow from O = softmax(S) V, S = scale Q K^T by the chain rule:
+//     dP = dO V^T,  dS_ij = P_ij (dP_ij - D_i),  D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic,
+//     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// With grouped K/V heads dK and dV of a K/V head sum over the query heads that read it; under
+// the causal mask the masked P_ij are 0.
+//
+// How it maps onto CDNA4. Three kernels, no atomics, every output written by one workgroup:
+//  * bwd_delta: D_i = sum_c dO_ic O_ic, one row per D/8 lanes.
+//  * bwd_dq: a workgroup owns 128 query rows of one (b, h) (32 per wave) and streams the head's
+//    K and V past them in 64-key tiles, exactly like the forward kernel: S^T = K Q^T and
+//    dP^T = V dO^T on 32x32x16 MFMAs with Q and dO held as B operands in registers, then in
+//    registers P^T and dS^T, and dQ^T += K^T dS^T with K^T read from LDS by transposing reads.
+//  * bwd_dkdv: a workgroup owns 128 keys of one (b, h_kv) (32 per wave) and streams the query
+//    rows of every query head of the group past them in 64-row tiles: S = Q K^T and dP = dO V^T
+//    with K and V held as B operands, P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS
+//    with dO^T and Q^T read by transposing reads.
+//  In both, the 32x32 accumulator of S (or S^T) splits into 8-value halves that are the B
+//  operands of the next 16-step MFMAs under the same fixed row permutation the forward kernel
+//  uses for P; the transposing reads follow it. P and dS are rounded to the input type (round to
+//  nearest even) only as MFMA operands; everything else is fp32.
+//  Tiles go from HBM straight into LDS (global_load_lds), two buffers, a quarter per wave, with
+//  the 16-byte-chunk swizzle chunk ^ (row / 2) % 8; both the row reads and the transposing reads
+//  of a tile use it.
+
+#include "fa_internal.h"
+#include "mfma_common.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kTile = 64;                        // keys (dQ) or query rows (dK, dV) per streamed tile
+constexpr int kOwn = kBwdWaves * 32;             // query rows (dQ) or keys (dK, dV) per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, typename T>
+struct BCfg {
+  typedef typename Mma<T>::v8 v8;
+  static constexpr int KS = D / 16;              // 16-wide k steps over the head dimension
+  static constexpr int DB = D / 32;              // 32-dim blocks of the gradient accumulators
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int ELEMS = kTile * D;        // elements per tile
+  static constexpr int LPW = ELEMS / 8 / 64 / kBwdWaves;  // 1 KB loads per wave and tile
+  static_assert(LPW >= 1 && LPW * 64 * kBwdWaves * 8 == ELEMS, "tile / wave mismatch");
+};
+
+// 4-byte-per-lane global -> LDS copy: lane i's 4 bytes land at lds + 4 * i.
+__device__ __forceinline__ void global_to_lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// HBM -> LDS of a 64-row tile, a quarter per wave. LDS chunk c of tile row r holds global chunk
+// c ^ swzk(r); rows at or past `nrows` repeat row nrows - 1 (their results are masked or never
+// stored).
+template <int D, typename T>
+__device__ __forceinline__ void load_tile(const T* __restrict__ X, T* lx, int row0, int nrows, int wave, int lane) {
+  typedef BCfg<D, T> C;
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int base = (wave * C::LPW + i) * 64;   // first LDS chunk of this load (wave-uniform)
+    const int ci = base + lane;
+    const int r = ci / C::CH, cpos = ci % C::CH;
+    const int row = min(row0 + r, nrows - 1);
+    global_to_lds16(X + (size_t)row * D + ((cpos ^ swzk(r)) << 3), &lx[base * 8]);
+  }
+}
+
+// 64 row values (lse or D) of rows row0.. into LDS; rows at or past nrows repeat the last one.
+__device__ __forceinline__ void load_rowvec(const float* __restrict__ x, float* lx, int row0, int nrows, int lane) {
+  global_to_lds4(x + min(row0 + lane, nrows - 1), lx);
+}
+
+// 16 bytes of tile row r, global chunk ch: an A or B operand row fragment.
+template <int D, typename T>
+__device__ __forceinline__ typename Mma<T>::v8 row_frag(const T* lx, int r, int ch) {
+  return *reinterpret_cast<const typename Mma<T>::v8*>(&lx[r * D + ((ch ^ swzk(r)) << 3)]);
+}
+
+// A operand X^T[dims of block db][rows of 16-step g] of a row-major tile X, read transposed, in
+// the row order of the P operands built by pack8 (the forward kernel's V^T read).
+template <int D, typename T>
+__device__ __forceinline__ typename Mma<T>::v8 tr_frag(const T* lx, int g, int db, int lane) {
+  const int hf = lane >> 5;
+  const int tj = lane & 15;
+  const int ti = tj >> 2;
+  const int tq = tj & 3;
+  const int tgb = (lane >> 4) & 1;
+  const int row1 = 16 * g + 4 * hf + ti;
+  const int col = db * 32 + tgb * 16 + tq * 4;
+  const int off1 = row1 * D + (((col >> 3) ^ swzk(row1)) << 3) + (col & 7);
+  const int off2 = (row1 + 8) * D + (((col >> 3) ^ swzk(row1 + 8)) << 3) + (col & 7);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off1]);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off2]);
+  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+  const u32x4_t packed = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(typename Mma<T>::v8, packed);
+}
+
+// B operand of 16-step g from the fp32 values x[32] of two 32-row accumulator blocks: values
+// 8g .. 8g+7 (block g / 2, registers 8 (g % 2) .. +7), rounded to T.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[32], int g) {
+  typename Mma<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (T)x[8 * g + i];
+  return r;
+}
+
+// Row index (within a 32-row block) of register r of lane half hf in a 32x32 accumulator.
+__device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// ---------------------------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic
+// ---------------------------------------------------------------------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, long long rows) {
+  constexpr int LPR = D / 8;                     // lanes per row, 8 elements each
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c0 = (threadIdx.x % LPR) * 8;
+  float s = 0.f;
+  if (row < rows) {
+    const size_t e = (size_t)row * D + c0;
+    const typename Mma<T>::v8 g = *reinterpret_cast<const typename Mma<T>::v8*>(static_cast<const T*>(a.dout) + e);
+    if (a.o_dtype == kF32) {
+      const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.o) + e);
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.o) + e + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = __builtin_fmaf((float)g[i], o0[i], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = __builtin_fmaf((float)g[4 + i], o1[i], s);
+    } else {
+      const typename Mma<T>::v8 o = *reinterpret_cast<const typename Mma<T>::v8*>(static_cast<const T*>(a.o) + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)g[i], (float)o[i], s);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
+  if (row < rows && c0 == 0) a.delta[row] = s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ: 128 query rows of one (b, h) per workgroup, K/V streamed in 64-key tiles
+// ---------------------------------------------------------------------------------------------
+template <int D, typename T, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  typedef BCfg<D, T> C;
+  typedef typename C::v8 v8;
+  __shared__ __attribute__((aligned(16))) T lds_k[2][C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v[2][C::ELEMS];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = CAUSAL ? n_qtiles - 1 - wg % n_qtiles : wg % n_qtiles;
+  const int rest = wg / n_qtiles;
+  const int h = rest % a.H;
+  const int b = rest / a.H;
+  const size_t head = (size_t)b * a.H + h;
+  const size_t kvh = kv_head_index(b, h, a.H, a.H_kv);
+  const T* __restrict__ Q = static_cast<const T*>(a.q) + head * (size_t)a.Nq * D;
+  const T* __restrict__ dO = static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int row = qt * kOwn + wave * 32 + l32;   // this lane's query row (column of S^T)
+  const int rowc = min(row, a.Nq - 1);
+
+  // Key range of the workgroup: under the mask it ends after the last key its last row sees.
+  int kend = a.Nk;
+  if constexpr (CAUSAL) kend = min(kend, min(a.Nq, (qt + 1) * kOwn) + a.causal_off);
+  const int T_ = (kend + kTile - 1) / kTile;
+
+  v8 qf[C::KS], dof[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)rowc * D + ks * 16 + hf * 8);
+    dof[ks] = *reinterpret_cast<const v8*>(dO + (size_t)rowc * D + ks * 16 + hf * 8);
+  }
+  const float L2 = a.lse[head * a.Nq + rowc] * kLog2e;
+  const float Dr = a.delta[head * a.Nq + rowc];
+  const float c2 = a.scale_log2e;
+  const int last_key = CAUSAL ? row + a.causal_off : a.Nk - 1;   // keys past it are masked
+
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  load_tile<D, T>(K, lds_k[0], 0, a.Nk, wave, lane);
+  load_tile<D, T>(V, lds_v[0], 0, a.Nk, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int t = 0; t < T_; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < T_) {
+      load_tile<D, T>(K, lds_k[cur ^ 1], (t + 1) * kTile, a.Nk, wave, lane);
+      load_tile<D, T>(V, lds_v[cur ^ 1], (t + 1) * kTile, a.Nk, wave, lane);
+    }
+    const T* lk = lds_k[cur];
+    const T* lv = lds_v[cur];
+    // S^T = K Q^T and dP^T = V dO^T: rows = the tile's 64 keys (two 32-blocks), columns = queries
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = Mma<T>::mma(row_frag<D, T>(lk, kb * 32 + l32, ks * 2 + hf), qf[ks], s[kb]);
+        dp[kb] = Mma<T>::mma(row_frag<D, T>(lv, kb * 32 + l32, ks * 2 + hf), dof[ks], dp[kb]);
+      }
+    // P^T = exp(S - L) (0 where masked) and dS^T = P^T (dP^T - D), per lane (one query)
+    float ds[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * kTile + kb * 32 + acc_row(r, hf);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
+        if (key > last_key) p = 0.f;
+        ds[kb * 16 + r] = p * (dp[kb][r] - Dr);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const v8 dsf = pack8<T>(ds, g);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag<D, T>(lk, g, db, lane), dsf, acc[db]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (row < a.Nq) {
+    float* out = a.dq + (head * (size_t)a.Nq + row) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = db * 32 + 8 * g4 + 4 * hf;
+        f32x4_t x = {a.scale * acc[db][4 * g4], a.scale * acc[db][4 * g4 + 1], a.scale * acc[db][4 * g4 + 2],
+                     a.scale * acc[db][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(out + dd) = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV: 128 keys of one (b, h_kv) per workgroup, query rows of the group streamed in 64-row tiles
+// ---------------------------------------------------------------------------------------------
+template <int D, typename T, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+  typedef BCfg<D, T> C;
+  typedef typename C::v8 v8;
+  __shared__ __attribute__((aligned(16))) T lds_q[2][C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do[2][C::ELEMS];
+  __shared__ __attribute__((aligned(16))) float lds_l[2][kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d[2][kTile];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = wg % n_ktiles;
+  const int rest = wg / n_ktiles;
+  const int hk = rest % a.H_kv;
+  const int b = rest / a.H_kv;
+  const int group = a.H / a.H_kv;
+  const size_t kvh = (size_t)b * a.H_kv + hk;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int key = kt * kOwn + wave * 32 + l32;   // this lane's key (column of S)
+  const int keyc = min(key, a.Nk - 1);
+
+  v8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)keyc * D + ks * 16 + hf * 8);
+    vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)keyc * D + ks * 16 + hf * 8);
+  }
+  const float c2 = a.scale_log2e;
+
+  f32x16_t dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
+
+  // Query tiles: those holding a row that sees the workgroup's first key (all of them unmasked).
+  const int n_rtiles = (a.Nq + kTile - 1) / kTile;
+  int r_begin = 0;
+  if constexpr (CAUSAL) r_begin = max(0, kt * kOwn - a.causal_off) / kTile;
+  const int per_head = n_rtiles - r_begin;
+  const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
+
+  auto issue = [&](int step, int buf) {
+    const int h = hk * group + step / per_head;
+    const int r0 = (r_begin + step % per_head) * kTile;
+    const size_t head = (size_t)b * a.H + h;
+    load_tile<D, T>(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lds_q[buf], r0, a.Nq, wave, lane);
+    load_tile<D, T>(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, lds_do[buf], r0, a.Nq, wave, lane);
+    if (wave == 0) load_rowvec(a.lse + head * a.Nq, lds_l[buf], r0, a.Nq, lane);
+    if (wave == 1) load_rowvec(a.delta + head * a.Nq, lds_d[buf], r0, a.Nq, lane);
+  };
+
+  if (n_steps > 0) issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int st = 0; st < n_steps; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < n_steps) issue(st + 1, cur ^ 1);
+    const int r0 = (r_begin + st % per_head) * kTile;
+    const T* lq = lds_q[cur];
+    const T* ldo = lds_do[cur];
+    // S = Q K^T and dP = dO V^T: rows = the tile's 64 query rows (two 32-blocks), columns = keys
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = Mma<T>::mma(row_frag<D, T>(lq, qb * 32 + l32, ks * 2 + hf), kf[ks], s[qb]);
+        dp[qb] = Mma<T>::mma(row_frag<D, T>(ldo, qb * 32 + l32, ks * 2 + hf), vf[ks], dp[qb]);
+      }
+    // P = exp(S - L) (0 for rows past Nq and masked keys), dS = P (dP - D)
+    float p[32], ds[32];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
+        const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&lds_l[cur][i0]);
+        const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&lds_d[cur][i0]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g4 + u;
+          const int qrow = r0 + i0 + u;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u] * kLog2e));
+          bool live = qrow < a.Nq;
+          if constexpr (CAUSAL) live = live && key <= qrow + a.causal_off;
+          if (!live) x = 0.f;
+          p[qb * 16 + r] = x;
+          ds[qb * 16 + r] = x * (dp[qb][r] - Dv[u]);
+        }
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const v8 pf = pack8<T>(p, g);
+      const v8 dsf = pack8<T>(ds, g);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        dv[db] = Mma<T>::mma(tr_frag<D, T>(ldo, g, db, lane), pf, dv[db]);
+        dk[db] = Mma<T>::mma(tr_frag<D, T>(lq, g, db, lane), dsf, dk[db]);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (key < a.Nk) {
+    float* outk = a.dk + (kvh * (size_t)a.Nk + key) * D;
+    float* outv = a.dv + (kvh * (size_t)a.Nk + key) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = db * 32 + 8 * g4 + 4 * hf;
+        f32x4_t xk = {a.scale * dk[db][4 * g4], a.scale * dk[db][4 * g4 + 1], a.scale * dk[db][4 * g4 + 2],
+                      a.scale * dk[db][4 * g4 + 3]};
+        f32x4_t xv = {dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(outk + dd) = xk;
+        *reinterpret_cast<f32x4_t*>(outv + dd) = xv;
+      }
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.H * a.Nq;
+  const long long nd = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+  const int n_qtiles = (a.Nq + kOwn - 1) / kOwn;
+  const int n_ktiles = (a.Nk + kOwn - 1) / kOwn;
+  const long long nq = (long long)n_qtiles * a.H * a.B;
+  const long long nk = (long long)n_ktiles * a.H_kv * a.B;
+  if (nd > 0x7fffffffLL || nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  BwdArgs args = a;
+  if (rows > 0) {  // D first (the other two kernels read it), then dQ, then dK and dV
+    long long r = rows;
+    void* kargs[] = {&args, &r};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, T>), dim3((unsigned)nd),
+                                   dim3(256), kargs, 0, s);
+    if (e != hipSuccess) return e;
+    int n = n_qtiles;
+    void* kargs2[] = {&args, &n};
+    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, true>)
+                             : reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, false>);
+    e = hipLaunchKernel(k, dim3((unsigned)nq), dim3(kBwdThreads), kargs2, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (nk == 0) return hipSuccess;
+  int n = n_ktiles;
+  void* kargs[] = {&args, &n};
+  const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, true>)
+                           : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, false>);
+  return hipLaunchKernel(k, dim3((unsigned)nk), dim3(kBwdThreads), kargs, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int d, int in_dtype, hipStream_t s) {
+  if (in_dtype == kBF16) {
+    if (d == 64) return launch_typed<64, __bf16>(a, s);
+    if (d == 128) return launch_typed<128, __bf16>(a, s);
+  } else if (in_dtype == kF16) {
+    if (d == 64) return launch_typed<64, _Float16>(a, s);
+    if (d == 128) return launch_typed<128, _Float16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

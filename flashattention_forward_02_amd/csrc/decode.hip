@@ -217,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
     if (a.split_mode == 0) {
       if (a.m_out) a.m_out[qrow] = m_nat;
       if (a.l_out) a.l_out[qrow] = L;
+      if (a.lse_out) a.lse_out[qrow] = m_nat + logf(L);
     } else {
       const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
       a.part_m[prow] = m_nat;

@@ -101,8 +101,8 @@ fa_status check_ext(const char* fn, int H, int H_kv, int Nq, int Nk, int causal)
 }
 
 fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out,
-                   int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype,
-                   fa_dtype out_dtype, void* stream) {
+                   float* lse_out, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                   fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
   fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
   if (st != FA_OK) return st;
   if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
@@ -110,7 +110,8 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
   if (out_dtype != FA_F32 && out_dtype != in_dtype)
     return fail(FA_EINVAL, "%s: out_dtype=%d must be FA_F32 or equal to in_dtype=%d", fn, (int)out_dtype, (int)in_dtype);
   if (!aligned16(o)) return fail(FA_EINVAL, "%s: o must be 16-byte aligned", fn);
-  if (!aligned4(m_out) || !aligned4(l_out)) return fail(FA_EINVAL, "%s: m_out and l_out must be 4-byte aligned", fn);
+  if (!aligned4(m_out) || !aligned4(l_out) || !aligned4(lse_out))
+    return fail(FA_EINVAL, "%s: m_out, l_out and lse must be 4-byte aligned", fn);
   if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
   const size_t obytes = (size_t)B * H * Nq * d * dtype_size(out_dtype);
   const size_t qbytes = (size_t)B * H * Nq * d * dtype_size(in_dtype);
@@ -122,6 +123,7 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
   a.o = o;
   a.m_out = m_out;
   a.l_out = l_out;
+  a.lse_out = lse_out;
   a.out_dtype = out_dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -166,16 +168,82 @@ extern "C" {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
                  int Nq, int Nk, int d, float scale, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
   g_last_error[0] = 0;
-  return fwd_impl("fa_fwd", q, k, v, o, m_out, l_out, B, H, H > 0 ? H : 1, Nq, Nk, d, scale, 0, in_dtype, out_dtype,
-                  stream);
+  return fwd_impl("fa_fwd", q, k, v, o, m_out, l_out, nullptr, B, H, H > 0 ? H : 1, Nq, Nk, d, scale, 0, in_dtype,
+                  out_dtype, stream);
 }
 
 fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* m_out, float* l_out, int B, int H,
                      int H_kv, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype, fa_dtype out_dtype,
                      void* stream) {
   g_last_error[0] = 0;
-  return fwd_impl("fa_fwd_ext", q, k, v, o, m_out, l_out, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, out_dtype,
-                  stream);
+  return fwd_impl("fa_fwd_ext", q, k, v, o, m_out, l_out, nullptr, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype,
+                  out_dtype, stream);
+}
+
+fa_status fa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+                     int Nk, int d, float scale, int causal, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (!lse && B > 0 && H > 0 && Nq > 0) return fail(FA_EINVAL, "fa_fwd_lse: lse must be a non-NULL device pointer");
+  return fwd_impl("fa_fwd_lse", q, k, v, o, nullptr, nullptr, lse, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype,
+                  out_dtype, stream);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 float* delta, float* dq, float* dk, float* dv, int B, int H, int H_kv, int Nq, int Nk, int d,
+                 float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+  g_last_error[0] = 0;
+  const char* fn = "fa_bwd";
+  fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
+  if (in_dtype == FA_F32) return fail(FA_EUNSUPPORTED, "%s: fp32 inputs (supported: FA_BF16, FA_F16)", fn);
+  if (o_dtype != FA_F32 && o_dtype != in_dtype)
+    return fail(FA_EINVAL, "%s: o_dtype=%d must be FA_F32 or equal to in_dtype=%d", fn, (int)o_dtype, (int)in_dtype);
+  const size_t nrows = (size_t)B * H * Nq;
+  if ((!o || !dout || !lse || !delta || !dq) && nrows != 0)
+    return fail(FA_EINVAL, "%s: o, dout, lse, delta and dq must be non-NULL device pointers", fn);
+  if ((!dk || !dv) && (size_t)B * H != 0) return fail(FA_EINVAL, "%s: dk and dv must be non-NULL device pointers", fn);
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) ||
+      !aligned4(delta))
+    return fail(FA_EINVAL, "%s: o, dout, dq, dk, dv must be 16-byte and lse, delta 4-byte aligned", fn);
+  if ((size_t)B * H == 0) return FA_OK;
+  // Outputs must not overlap any input or each other.
+  const size_t qb = nrows * d * 2, kvb = (size_t)B * H_kv * Nk * d * 2, ob = nrows * d * dtype_size(o_dtype);
+  const size_t qf = nrows * d * 4, kvf = (size_t)B * H_kv * Nk * d * 4, rb = nrows * 4;
+  const void* ins[] = {q, k, v, o, dout, lse};
+  const size_t insz[] = {qb, kvb, kvb, ob, qb, rb};
+  const void* outs[] = {delta, dq, dk, dv};
+  const size_t outsz[] = {rb, qf, kvf, kvf};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return fail(FA_EINVAL, "%s: an output overlaps an input", fn);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return fail(FA_EINVAL, "%s: two outputs overlap", fn);
+  }
+  fa::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.causal = causal;
+  a.causal_off = Nk - Nq;
+  a.o_dtype = o_dtype;
+  a.scale = scale;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  // (Nq = 0 launches only the dK / dV kernel, which then writes zeros.)
+  return launched(fn, fa::launch_bwd(a, d, in_dtype, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,

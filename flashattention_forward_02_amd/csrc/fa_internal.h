@@ -18,6 +18,7 @@ struct FwdArgs {
   void* o;
   float* m_out;
   float* l_out;
+  float* lse_out;   // optional row log-sum-exp m + ln(l) (full mode)
   float* part_m;
   float* part_l;
   float* part_o;
@@ -65,7 +66,26 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   return (wg & 7) * (nwg >> 3) + (wg >> 3);
 }
 
+// Backward arguments (bf16 / fp16 inputs; gradients in fp32).
+struct BwdArgs {
+  const void* q;      // [B, H, Nq, d] in_dtype
+  const void* k;      // [B, H_kv, Nk, d] in_dtype
+  const void* v;      // [B, H_kv, Nk, d] in_dtype
+  const void* o;      // [B, H, Nq, d] o_dtype (forward output)
+  const void* dout;   // [B, H, Nq, d] in_dtype
+  const float* lse;   // [B, H, Nq] row log-sum-exp of the scaled scores
+  float* delta;       // [B, H, Nq] workspace: D_i = sum_c dO_ic O_ic
+  float* dq;          // [B, H, Nq, d]
+  float* dk;          // [B, H_kv, Nk, d]
+  float* dv;          // [B, H_kv, Nk, d]
+  int B, H, H_kv, Nq, Nk;
+  int causal, causal_off;
+  int o_dtype;
+  float scale, scale_log2e;
+};
+
 hipError_t launch_fwd_mfma(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t s);

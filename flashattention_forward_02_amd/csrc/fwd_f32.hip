@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
     if (col0 == 0) {
       if (a.m_out) a.m_out[head * a.Nq + row] = m;
       if (a.l_out) a.l_out[head * a.Nq + row] = l;
+      if (a.lse_out) a.lse_out[head * a.Nq + row] = m + logf(l);
     }
   } else {
     const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;

@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of libfa.so, a FlashAttention forward pass for AMD MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so, a FlashAttention forward pass (and its gradients) for AMD MI355X
+ * (gfx950).
  *
  * The operation (one attention head; every (b, h) pair is independent):
  *
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 #define FA_MAX_SPLITS 256
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
@@ -110,6 +111,48 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o,
                      float* m_out, float* l_out,
                      int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
                      fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_lse -- fa_fwd_ext that also stores each row's log-sum-exp, the statistic the backward
+ * pass needs.
+ *
+ * "Flash Attention 代码填空 (Level 2-3)" Exercise 5 keeps the row statistics m and l of the
+ * forward pass so that the backward pass can recompute P without storing it; "CS349E 第 11 讲
+ * 01_online_softmax.py" notes that FlashAttention-2 keeps a single number per row instead, the
+ * log-sum-exp L = m + ln(l), from which P_ij = exp(S_ij - L_i).
+ *   lse  [B,H,Nq] fp32, receives L_i = m_i + ln(l_i) of the scaled scores S (natural log).
+ * Everything else as in fa_fwd_ext (this call computes the running maximum exactly).
+ */
+fa_status fa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                     fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_bwd -- gradients of O = softmax(scale * Q K^T) V with respect to Q, K and V.
+ *
+ * "Flash Attention 代码填空 (Level 2-3)" Exercise 5: the backward pass recomputes P from the
+ * stored row statistics, P_ij = exp(S_ij - L_i), and accumulates dV_j = sum_i P_ij^T dO_i; the
+ * other two gradients follow from the same definition by the chain rule
+ * ("FlashAttention 简化版：Tiling + Online Softmax" §7 lists the backward pass, recomputation
+ * plus blockwise gradients, as the first extension):
+ *     dP = dO V^T,   dS_ij = P_ij (dP_ij - D_i),   D_i = sum_c dO_ic O_ic,
+ *     dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+ *   q, k, v   the forward inputs (layouts and H_kv, causal as in fa_fwd_ext), FA_BF16 or FA_F16.
+ *   o         [B,H,Nq,d] the forward output, in o_dtype (FA_F32 or in_dtype).
+ *   dout      [B,H,Nq,d] dL/dO, in in_dtype.
+ *   lse       [B,H,Nq] fp32 row log-sum-exp from fa_fwd_lse (same q, k, scale, causal).
+ *   delta     [B,H,Nq] fp32 workspace owned by the caller; receives D_i.
+ *   dq        [B,H,Nq,d] fp32; dk, dv [B,H_kv,Nk,d] fp32. With grouped heads dk and dv of a
+ *             K/V head sum over the query heads that read it.
+ * No [Nq, Nk] matrix is stored: P and dS are recomputed tile by tile, rounded to in_dtype only
+ * as matrix-core operands, and accumulated in fp32. Every output element is written by exactly
+ * one workgroup (no atomics), so results are bitwise reproducible. Outputs must not overlap any
+ * input or each other. fp32 inputs return FA_EUNSUPPORTED. Nq = 0 gives dk = dv = 0.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, float* delta, float* dq, float* dk, float* dv,
+                 int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                 fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
 
 /*
  * fa_fwd_split_ext -- fa_fwd_split with grouped K/V heads and an optional causal mask.

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert n.fa_abi_version() == 2
+    assert n.fa_abi_version() == 3
     assert [n.fa_status_string(s) for s in range(4)] == ["FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
     assert n.fa_status_string(99) == "FA_UNKNOWN_STATUS"
 
@@ -185,3 +185,64 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
             assert not re.search(r"^\s*(from|import)\s+(oracle|seeded_inputs)", src, flags=re.M), name
             for op in (".softmax(", "einsum(", "matmul(", "scaled_dot_product_attention", ".exp(", " @ "):
                 assert op not in src, (name, op)
+
+
+def fwd_lse(**kw):
+    a = dict(q=P, k=P, v=P, o=P * 2, lse=P * 3, B=1, H=2, H_kv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=1,
+             in_dtype=n.FA_BF16, out_dtype=n.FA_F32, stream=None)
+    a.update(kw)
+    return n.fa_fwd_lse(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(lse=None), n.FA_EINVAL, "lse"),
+    (dict(lse=P * 3 + 2), n.FA_EINVAL, "aligned"),
+    (dict(H_kv=3), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(Nq=9), n.FA_EINVAL, "Nq <= Nk"),
+    (dict(causal=2), n.FA_EINVAL, "causal"),
+    (dict(d=32), n.FA_EUNSUPPORTED, "d=32"),
+])
+def test_fa_fwd_lse_rejects(kw, status, msg):
+    assert fwd_lse(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_fa_fwd_lse_empty_work_is_ok_without_device():
+    assert fwd_lse(Nq=0, lse=None) == n.FA_OK
+    assert fwd_lse(B=0, q=None, k=None, v=None, o=None, lse=None) == n.FA_OK
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P * 2, v=P * 3, o=P * 4, dout=P * 5, lse=P * 6, delta=P * 7, dq=P * 8, dk=P * 9, dv=P * 10,
+             B=1, H=2, H_kv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, in_dtype=n.FA_BF16, o_dtype=n.FA_F32,
+             stream=None)
+    a.update(kw)
+    return n.fa_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(in_dtype=n.FA_F32), n.FA_EUNSUPPORTED, "fp32 inputs"),
+    (dict(o_dtype=n.FA_F16), n.FA_EINVAL, "o_dtype"),
+    (dict(dout=None), n.FA_EINVAL, "non-NULL"),
+    (dict(lse=None), n.FA_EINVAL, "non-NULL"),
+    (dict(delta=None), n.FA_EINVAL, "non-NULL"),
+    (dict(dk=None), n.FA_EINVAL, "non-NULL"),
+    (dict(dq=P * 8 + 4), n.FA_EINVAL, "aligned"),
+    (dict(lse=P * 6 + 2), n.FA_EINVAL, "aligned"),
+    (dict(dq=P), n.FA_EINVAL, "overlaps an input"),
+    (dict(dk=P * 8), n.FA_EINVAL, "two outputs overlap"),
+    (dict(H_kv=3), n.FA_EINVAL, "multiple of H_kv"),
+    (dict(causal=1, Nq=9), n.FA_EINVAL, "Nq <= Nk"),
+    (dict(Nk=0), n.FA_EINVAL, "empty key set"),
+    (dict(d=96), n.FA_EUNSUPPORTED, "d=96"),
+    (dict(scale=-0.5), n.FA_EINVAL, "scale"),
+])
+def test_fa_bwd_rejects(kw, status, msg):
+    assert bwd(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_fa_bwd_empty_batch_is_ok_without_device():
+    assert bwd(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, delta=None, dq=None, dk=None,
+               dv=None) == n.FA_OK
+    assert n.fa_last_error() == ""
