@@ -1,10 +1,11 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload headline|long_seq|causal|decode|gqa_decode] [--no-cpu]
+                    [--workload headline|long_seq|causal|decode|gqa_decode|bwd] [--no-cpu]
 
-A step is one forward over the whole batch (headline, long_seq, causal) or one split + merge pair
-(decode, gqa_decode). Inputs are generated and resident in HBM before the timed region. Prints ONE
+A step is one forward over the whole batch (headline, long_seq, causal), one split + merge pair
+(decode, gqa_decode), or one backward call over the whole batch (bwd: dQ, dK, dV from the stored
+log-sum-exp; the forward that produces O and it runs once before the timed region). Inputs are generated and resident in HBM before the timed region. Prints ONE
 JSON line. The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per
 step); the causal workload counts 4*d flops per visible (query, key) pair.
 """
@@ -30,7 +31,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="headline", choices=["headline", "long_seq", "causal", "decode", "gqa_decode"])
+    p.add_argument("--workload", default="headline",
+                   choices=["headline", "long_seq", "causal", "decode", "gqa_decode", "bwd"])
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
@@ -87,6 +89,36 @@ def cpu_baseline(w, q, k, v, o_gpu, max_heads):
             {"max_abs": max_abs, "rel_l2": rel, "heads_checked": done})
 
 
+def cpu_baseline_bwd(w, q, k, v, do, grads, max_heads):
+    """Time the fp64 gradient oracle on a bounded sample of whole heads of the same workload, on this host."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    from threadpoolctl import threadpool_info
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+    errs = []
+    t0 = time.perf_counter()
+    done = 0
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_backward_fp64(*(si.torch_to_f64(x[sl]) for x in (q, k, v, do)), w.scale)[:3]
+        for g, r in zip(grads, ref):
+            got = si.torch_to_f64(g[sl])
+            errs.append((float(np.max(np.abs(got - r))), float(np.linalg.norm(got - r)), float(np.linalg.norm(r))))
+        done += 1
+        if time.perf_counter() - t0 > 20.0:
+            break
+    dt = time.perf_counter() - t0
+    flops = 10.0 * done * w.Nq * w.Nk * w.d
+    rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / (sum(e[2] ** 2 for e in errs) ** 0.5)
+    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+             "sample": f"{done} of {w.B * w.H} heads (dQ, dK, dV of all {w.Nq} rows) of the same inputs, "
+                       f"{dt:.1f} s wall, fp64 numpy"},
+            {"max_abs": max(e[0] for e in errs), "rel_l2": rel, "heads_checked": done})
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,7 +133,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16,
-          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16}[args.workload]
+          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16, "bwd": si.BWD_BF16}[args.workload]
+    is_bwd = args.workload == "bwd"
     is_decode = args.workload in ("decode", "gqa_decode")
 
     if is_decode:
@@ -110,6 +143,8 @@ def main():
         qh, kh, vh = si.workload_inputs(wl)
         q, k, v = qh.to_torch(dev), kh.to_torch(dev), vh.to_torch(dev)
         del qh, kh, vh
+        if is_bwd:
+            dout = si.grad_output(wl).to_torch(dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -136,6 +171,19 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
             fa.merge_states(pm, pl, po, order=order, out=o)
+    elif is_bwd:
+        o, lse = fa.fwd_lse(q, k, v, scale=wl.scale)
+        grads = (torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32),
+                 torch.empty(k.shape, device=dev, dtype=torch.float32),
+                 torch.empty(k.shape, device=dev, dtype=torch.float32),
+                 torch.empty((wl.B, wl.H, wl.Nq), device=dev, dtype=torch.float32))
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fa.bwd(q, k, v, o, dout, lse, scale=wl.scale, out=grads)
+            if ev is not None:
+                ev[1].record(stream)
     else:
         o = torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32)
 
@@ -188,6 +236,18 @@ def main():
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                               **launch_stats, "traffic": traffic_for(args.workload, source_hash("decode.hip"))}
         result["step_bytes"] = step_bytes
+    elif is_bwd:
+        flops = 10.0 * wl.B * wl.H * wl.Nq * wl.Nk * wl.d
+        result.update({"metric": ("FA bwd TFLOP/s (10*B*H*N^2*d: the products S, dP, dV, dK, dQ) at N=4096,d=64 "
+                                  "bf16; % of MFMA peak"), "unit": "TFLOP/s",
+                       "value": flops / (ms_per_step * 1e-3) / 1e12,
+                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
+                                  "causal": False, "grad_dtype": "fp32"}})
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "kernel": "fa_bwd (bwd_delta + bwd_dq + bwd_dkdv)",
+                              "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
+                              "traffic": traffic_for("bwd", source_hash("bwd.hip"))}
     else:
         flops = wl.flops
         tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -208,6 +268,10 @@ def main():
 
     if not args.no_cpu and args.workload == "headline":
         base, check = cpu_baseline(wl, q, k, v, o, max_heads=wl.B * wl.H)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = check
+    if not args.no_cpu and is_bwd:
+        base, check = cpu_baseline_bwd(wl, q, k, v, dout, grads[:3], max_heads=wl.B * wl.H)
         result["cpu_baseline"] = base
         result["parity_sample"] = check
     print(json.dumps(result), flush=True)

@@ -173,12 +173,13 @@ def fwd_lse(q, k, v, scale=None, out_dtype=None, causal=False, out=None):
     return out, lse
 
 
-def bwd(q, k, v, o, dout, lse, scale=None, causal=False, return_delta=False):
+def bwd(q, k, v, o, dout, lse, scale=None, causal=False, return_delta=False, out=None):
     """(dq, dk, dv), fp32, of O = softmax(scale q k^T) v given dL/dO. See fa_bwd.
 
     ``o`` and ``lse`` come from ``fwd_lse`` on the same inputs; ``dout`` has q's dtype (bf16 or fp16).
     dk and dv have k's shape (with grouped K/V heads they sum over the query heads of a group).
-    With ``return_delta`` also returns D = rowsum(dout * o), fp32 [B,H,Nq].
+    With ``return_delta`` also returns D = rowsum(dout * o), fp32 [B,H,Nq]. ``out`` = (dq, dk, dv, delta)
+    supplies the four output buffers (contiguous float32 of those shapes) instead of allocating them.
     """
     torch = _torch()
     _check_qkv(q, k, v)
@@ -193,10 +194,16 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal=False, return_delta=False):
             raise TypeError(f"{name} must have q's dtype")
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
-    dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out is None:
+        dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, delta = out
+        for t, shp in ((dq, (B, H, Nq, d)), (dk, tuple(k.shape)), (dv, tuple(k.shape)), (delta, (B, H, Nq))):
+            if tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("out must be contiguous float32 (dq, dk, dv, delta) of the documented shapes")
     _native.check(_native.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                                  lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                  B, H, k.shape[1], Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q.dtype),

@@ -103,13 +103,13 @@ __device__ __forceinline__ typename Mma<T>::v8 tr_frag(const T* lx, int g, int d
   return __builtin_bit_cast(typename Mma<T>::v8, packed);
 }
 
-// B operand of 16-step g from the fp32 values x[32] of two 32-row accumulator blocks: values
-// 8g .. 8g+7 (block g / 2, registers 8 (g % 2) .. +7), rounded to T.
+// Eight fp32 values rounded to T: one B operand of a 16-step (values i = 0..7 are registers
+// 8 (g % 2) + i of the accumulator block g / 2, the row order the transposing reads follow).
 template <typename T>
-__device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[32], int g) {
+__device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[8]) {
   typename Mma<T>::v8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (T)x[8 * g + i];
+  for (int i = 0; i < 8; ++i) r[i] = (T)x[i];
   return r;
 }
 
@@ -153,8 +153,12 @@ template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   typedef BCfg<D, T> C;
   typedef typename C::v8 v8;
-  __shared__ __attribute__((aligned(16))) T lds_k[2][C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][C::ELEMS];
+  // Two separate buffers per tensor (not one array of two): a load into one is then seen not to
+  // alias reads of the other, and reads of the current tile do not wait for the next tile's loads.
+  __shared__ __attribute__((aligned(16))) T lds_k0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_k1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v1[C::ELEMS];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = CAUSAL ? n_qtiles - 1 - wg % n_qtiles : wg % n_qtiles;
@@ -197,19 +201,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  load_tile<D, T>(K, lds_k[0], 0, a.Nk, wave, lane);
-  load_tile<D, T>(V, lds_v[0], 0, a.Nk, wave, lane);
+  load_tile<D, T>(K, lds_k0, 0, a.Nk, wave, lane);
+  load_tile<D, T>(V, lds_v0, 0, a.Nk, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = 0; t < T_; ++t) {
-    const int cur = t & 1;
+  // One key tile: prefetch tile t + 1 into (nk, nv), compute from (lk, lv), wait, barrier.
+  auto tile = [&](int t, const T* lk, const T* lv, T* nk, T* nv) __attribute__((always_inline)) {
     if (t + 1 < T_) {
-      load_tile<D, T>(K, lds_k[cur ^ 1], (t + 1) * kTile, a.Nk, wave, lane);
-      load_tile<D, T>(V, lds_v[cur ^ 1], (t + 1) * kTile, a.Nk, wave, lane);
+      load_tile<D, T>(K, nk, (t + 1) * kTile, a.Nk, wave, lane);
+      load_tile<D, T>(V, nv, (t + 1) * kTile, a.Nk, wave, lane);
     }
-    const T* lk = lds_k[cur];
-    const T* lv = lds_v[cur];
     // S^T = K Q^T and dP^T = V dO^T: rows = the tile's 64 keys (two 32-blocks), columns = queries
     f32x16_t s[2], dp[2];
 #pragma unroll
@@ -223,26 +225,30 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
         s[kb] = Mma<T>::mma(row_frag<D, T>(lk, kb * 32 + l32, ks * 2 + hf), qf[ks], s[kb]);
         dp[kb] = Mma<T>::mma(row_frag<D, T>(lv, kb * 32 + l32, ks * 2 + hf), dof[ks], dp[kb]);
       }
-    // P^T = exp(S - L) (0 where masked) and dS^T = P^T (dP^T - D), per lane (one query)
-    float ds[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t * kTile + kb * 32 + acc_row(r, hf);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
-        if (key > last_key) p = 0.f;
-        ds[kb * 16 + r] = p * (dp[kb][r] - Dr);
-      }
+    // per 16-key step g: P^T = exp(S - L) (0 where masked), dS^T = P^T (dP^T - D), then
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const v8 dsf = pack8<T>(ds, g);
+      const int kb = g >> 1;
+      float ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * (g & 1) + i;
+        const int key = t * kTile + kb * 32 + acc_row(r, hf);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
+        if (key > last_key) p = 0.f;
+        ds[i] = p * (dp[kb][r] - Dr);
+      }
+      const v8 dsf = pack8<T>(ds);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag<D, T>(lk, g, db, lane), dsf, acc[db]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int t = 0; t < T_; t += 2) {
+    tile(t, lds_k0, lds_v0, lds_k1, lds_v1);
+    if (t + 1 < T_) tile(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
 
   if (row < a.Nq) {
@@ -263,13 +269,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
 // dK, dV: 128 keys of one (b, h_kv) per workgroup, query rows of the group streamed in 64-row tiles
 // ---------------------------------------------------------------------------------------------
 template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+__global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   typedef BCfg<D, T> C;
   typedef typename C::v8 v8;
-  __shared__ __attribute__((aligned(16))) T lds_q[2][C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_do[2][C::ELEMS];
-  __shared__ __attribute__((aligned(16))) float lds_l[2][kTile];
-  __shared__ __attribute__((aligned(16))) float lds_d[2][kTile];
+  // Separate buffers per tensor and parity (see bwd_dq_kernel).
+  __shared__ __attribute__((aligned(16))) T lds_q0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_q1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) float lds_l0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_l1[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = wg % n_ktiles;
@@ -309,26 +320,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int
   const int per_head = n_rtiles - r_begin;
   const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
 
-  auto issue = [&](int step, int buf) {
+  auto issue = [&](int step, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
     const int h = hk * group + step / per_head;
     const int r0 = (r_begin + step % per_head) * kTile;
     const size_t head = (size_t)b * a.H + h;
-    load_tile<D, T>(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lds_q[buf], r0, a.Nq, wave, lane);
-    load_tile<D, T>(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, lds_do[buf], r0, a.Nq, wave, lane);
-    if (wave == 0) load_rowvec(a.lse + head * a.Nq, lds_l[buf], r0, a.Nq, lane);
-    if (wave == 1) load_rowvec(a.delta + head * a.Nq, lds_d[buf], r0, a.Nq, lane);
+    load_tile<D, T>(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lq, r0, a.Nq, wave, lane);
+    load_tile<D, T>(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, ldo, r0, a.Nq, wave, lane);
+    if (wave == 0) load_rowvec(a.lse + head * a.Nq, ll, r0, a.Nq, lane);
+    if (wave == 1) load_rowvec(a.delta + head * a.Nq, ld, r0, a.Nq, lane);
   };
 
-  if (n_steps > 0) issue(0, 0);
+  if (n_steps > 0) issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int st = 0; st < n_steps; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < n_steps) issue(st + 1, cur ^ 1);
+  // One (query head, row tile) step: prefetch the next into the other buffers, compute, wait, barrier.
+  auto step = [&](int st, const T* lq, const T* ldo, const float* ll, const float* ld, T* nq, T* ndo, float* nl,
+                  float* nd) __attribute__((always_inline)) {
+    if (st + 1 < n_steps) issue(st + 1, nq, ndo, nl, nd);
     const int r0 = (r_begin + st % per_head) * kTile;
-    const T* lq = lds_q[cur];
-    const T* ldo = lds_do[cur];
     // S = Q K^T and dP = dO V^T: rows = the tile's 64 query rows (two 32-blocks), columns = keys
     f32x16_t s[2], dp[2];
 #pragma unroll
@@ -342,15 +352,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int
         s[qb] = Mma<T>::mma(row_frag<D, T>(lq, qb * 32 + l32, ks * 2 + hf), kf[ks], s[qb]);
         dp[qb] = Mma<T>::mma(row_frag<D, T>(ldo, qb * 32 + l32, ks * 2 + hf), vf[ks], dp[qb]);
       }
-    // P = exp(S - L) (0 for rows past Nq and masked keys), dS = P (dP - D)
-    float p[32], ds[32];
+    // per 16-row step g: P = exp(S - L) (0 for rows past Nq and masked keys), dS = P (dP - D),
+    // then dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int g = 0; g < 4; ++g) {
+      const int qb = g >> 1;
+      float p[8], ds[8];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int g4 = 2 * (g & 1) + h2;
         const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
-        const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&lds_l[cur][i0]);
-        const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&lds_d[cur][i0]);
+        const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&ll[i0]);
+        const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&ld[i0]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g4 + u;
@@ -359,15 +372,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int
           bool live = qrow < a.Nq;
           if constexpr (CAUSAL) live = live && key <= qrow + a.causal_off;
           if (!live) x = 0.f;
-          p[qb * 16 + r] = x;
-          ds[qb * 16 + r] = x * (dp[qb][r] - Dv[u]);
+          p[4 * h2 + u] = x;
+          ds[4 * h2 + u] = x * (dp[qb][r] - Dv[u]);
         }
       }
-    // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const v8 pf = pack8<T>(p, g);
-      const v8 dsf = pack8<T>(ds, g);
+      const v8 pf = pack8<T>(p);
+      const v8 dsf = pack8<T>(ds);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
         dv[db] = Mma<T>::mma(tr_frag<D, T>(ldo, g, db, lane), pf, dv[db]);
@@ -376,6 +386,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int st = 0; st < n_steps; st += 2) {
+    step(st, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+    if (st + 1 < n_steps) step(st + 1, lds_q1, lds_do1, lds_l1, lds_d1, lds_q0, lds_do0, lds_l0, lds_d0);
   }
 
   if (key < a.Nk) {

@@ -180,6 +180,8 @@ HEADLINE_BF16 = Workload("headline B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096
 LONG_SEQ_BF16 = Workload("long_seq B=1 H=32 N=16384 d=128 bf16 Kx3", 1, 32, 16384, 16384, 128, "bf16", 4,
                          k_mult=3.0)
 CAUSAL_BF16 = Workload("causal B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096, 64, "bf16", 3, causal=True)
+# The backward pass on the headline inputs; dL/dO is tensor 3 of the same per-head draws.
+BWD_BF16 = Workload("backward B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 64, "bf16", 3)
 GQA_DECODE_BF16 = Workload("gqa_decode B=16 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 6,
                            num_splits=16, H_kv=8)
 DECODE_BF16 = Workload("split_kv_decode B=16 H=32 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 5,
@@ -222,6 +224,11 @@ def workload_inputs(w: Workload):
     k = per_head_tensor(w.seed, w.B, w.kv_heads, w.Nk, w.d, 1, w.dtype, w.k_mult)
     v = per_head_tensor(w.seed, w.B, w.kv_heads, w.Nk, w.d, 2, w.dtype)
     return q, k, v
+
+
+def grad_output(w: Workload):
+    """Host dL/dO [B, H, Nq, d] for a per-head-drawn workload (tensor index 3 of the same seed)."""
+    return per_head_tensor(w.seed, w.B, w.H, w.Nq, w.d, 3, w.dtype)
 
 
 def small_case(seed: int, B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, k_mult: float = 1.0):
