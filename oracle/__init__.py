@@ -26,6 +26,9 @@ What each function is pinned against (tests/test_oracle_pins.py):
   the 1e-16 level the lecture-11 demo 1 reports.
 * ``partial_state`` / ``merge_states`` / ``merge_*`` -- order independence at the
   1e-16 level the lecture-11 demo 2 reports, on the demo's own draws; empty states.
+* ``partial_state_lse`` / ``merge_lse`` (the (lse, o / l) form) -- the merged output against
+  full attention and the merged lse against scipy's logsumexp, on demo 2's own draws and
+  under the causal mask; order independence; empty and single-part states.
 * ``fa1_order_attention`` -- the delayed-normalisation form.
 * ``round_to_bf16`` / ``round_to_f16`` -- torch's and numpy's casts; the
   relative P.V error magnitudes the lecture-11 demo 4 reports.
@@ -65,6 +68,9 @@ from .attention import (  # noqa: F401
     finish_state,
     split_bounds,
     split_partial_states,
+    partial_state_lse,
+    merge_lse,
+    split_partial_states_lse,
     brute_force_attention,
     round_to_bf16,
     round_to_f16,

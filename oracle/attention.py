@@ -410,6 +410,68 @@ def split_partial_states(q, k, v, scale, num_splits: int, causal: bool = False):
 
 
 # ---------------------------------------------------------------------------
+# The (lse, o) form of a partial state (flash-decoding)
+# ---------------------------------------------------------------------------
+
+def partial_state_lse(s, V):
+    """(lse, o_n) of one segment of score rows: lse = m + ln(l), o_n = o / l.
+
+    [CS349E-L11], the note after demo 2: flash-decoding stores per segment the output already
+    divided by the segment's own l and lse_s = m_s + log l_s (one value fewer than (m, l, o)).
+    ``s`` is [rows, n], V [n, dv]. A row with no keys (empty segment, or all scores -inf) gets
+    (-inf, 0).
+    """
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    V = np.asarray(V, dtype=np.float64)
+    rows, dv = s.shape[0], V.shape[1]
+    lse = np.full(rows, NEG_INF)
+    on = np.zeros((rows, dv))
+    if s.shape[1] == 0:
+        return lse, on
+    m = s.max(axis=1)
+    live = np.isfinite(m)
+    p = np.exp(s[live] - m[live, None])
+    l = p.sum(axis=1)
+    lse[live] = m[live] + np.log(l)
+    on[live] = (p @ V) / l[:, None]
+    return lse, on
+
+
+def merge_lse(states, order=None):
+    """Combine (lse_s, o_s) states: lse = ln(sum_s exp(lse_s)), O = sum_s exp(lse_s - lse) o_s.
+
+    [CS349E-L11] (note after demo 2): the parts are weighted by exp(lse_s - lse). The log-sum-exp is
+    taken as max_s lse_s + ln(sum_s exp(lse_s - max)); both sums run in ``order`` (a permutation of
+    the state indices; default ascending). Empty parts (lse_s = -inf) weigh 0; a row whose parts
+    are all empty gets O = 0 and lse = -inf.
+    """
+    idx = list(range(len(states))) if order is None else [int(i) for i in order]
+    L = np.stack([np.asarray(states[i][0], dtype=np.float64) for i in idx])        # [S, rows]
+    O = np.stack([np.asarray(states[i][1], dtype=np.float64) for i in idx])        # [S, rows, dv]
+    mx = L.max(axis=0)
+    live = np.isfinite(mx)
+    w = np.zeros_like(L)
+    fin = np.isfinite(L) & live[None, :]
+    w[fin] = np.exp(L[fin] - np.broadcast_to(mx, L.shape)[fin])
+    lse = np.full(mx.shape, NEG_INF)
+    lse[live] = mx[live] + np.log(w[:, live].sum(axis=0))
+    wt = np.zeros_like(L)
+    wt[fin] = np.exp(L[fin] - np.broadcast_to(lse, L.shape)[fin])
+    out = (wt[..., None] * O).sum(axis=0)
+    return lse, out
+
+
+def split_partial_states_lse(q, k, v, scale, num_splits: int, causal: bool = False):
+    """Per-split (lse, o / l) for one head over ``split_bounds`` (the causal mask as in ``split_partial_states``)."""
+    s = scores_fp64(q, k, scale)
+    if causal:
+        last = causal_last_key(np.arange(s.shape[0]), s.shape[0], s.shape[1])
+        s = np.where(np.arange(s.shape[1])[None, :] <= last[:, None], s, NEG_INF)
+    v = np.asarray(v, dtype=np.float64)
+    return [partial_state_lse(s[:, a:b], v[a:b]) for a, b in split_bounds(k.shape[0], num_splits)]
+
+
+# ---------------------------------------------------------------------------
 # Brute force for tiny inputs
 # ---------------------------------------------------------------------------
 

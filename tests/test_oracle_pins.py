@@ -443,3 +443,54 @@ def test_causal_split_states_merge_to_causal_attention():
     for order in (None, list(range(7, -1, -1)), [3, 0, 6, 1, 7, 2, 5, 4]):
         got = oracle.finish_state(oracle.merge_sequential(states, order))
         assert np.max(np.abs(got - ref)) < 1e-14
+
+
+# --- the (lse, o) partial-state form ([CS349E-L11], the note after demo 2) -----------------------
+
+def test_lse_form_merge_demo2():
+    """The demo's own segmentation recipe (default_rng(1), S=3000, d=32, x*3, 12 random segments): the
+    (lse, o / l) states merged in three orders equal the one-shot output, and the merged lse equals
+    scipy's logsumexp of the row (the page calls the two encodings equivalent)."""
+    rng = np.random.default_rng(1)
+    S, d = 3000, 32
+    x = rng.standard_normal(S) * 3
+    V = rng.standard_normal((S, d))
+    cuts = np.sort(rng.choice(np.arange(1, S), size=11, replace=False))
+    bounds = list(zip(np.concatenate([[0], cuts]), np.concatenate([cuts, [S]])))
+    states = [oracle.partial_state_lse(x[None, a:b], V[a:b]) for a, b in bounds]
+    ref = scipy.special.softmax(x) @ V
+    for order in (None, rng.permutation(len(states)), list(range(len(states)))[::-1]):
+        lse, out = oracle.merge_lse(states, order)
+        assert np.max(np.abs(out[0] - ref)) < 1e-14
+        assert abs(lse[0] - scipy.special.logsumexp(x)) < 1e-12
+
+
+@pytest.mark.parametrize("Nq,Nk,S,causal", [(7, 50, 4, False), (30, 30, 5, True), (9, 40, 8, True)])
+def test_lse_form_split_matches_attention(Nq, Nk, S, causal):
+    r = _rng(40 + Nk)
+    q, k, v = r.standard_normal((Nq, 16)), r.standard_normal((Nk, 16)), r.standard_normal((Nk, 16))
+    states = oracle.split_partial_states_lse(q, k, v, 0.3, S, causal=causal)
+    lse, out = oracle.merge_lse(states, _rng(5).permutation(S))
+    ref = oracle.attention_fp64(q[None], k[None], v[None], 0.3, causal=causal)[0]
+    assert np.max(np.abs(out - ref)) < 1e-13
+    s = 0.3 * q @ k.T
+    if causal:
+        s = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq), s, -np.inf)
+    assert np.max(np.abs(lse - scipy.special.logsumexp(s, axis=1))) < 1e-12
+    if causal:  # some parts hold no visible key for the first rows: (-inf, 0)
+        assert any(np.any(np.isneginf(st[0])) for st in states)
+
+
+def test_lse_form_empty_and_single_states():
+    r = _rng(9)
+    V = r.standard_normal((6, 4))
+    s = r.standard_normal((3, 6))
+    one = oracle.partial_state_lse(s, V)
+    empty = oracle.partial_state_lse(s[:, :0], V[:0])
+    assert np.all(np.isneginf(empty[0])) and np.all(empty[1] == 0)
+    for states in ([one], [empty, one], [one, empty, empty]):
+        lse, out = oracle.merge_lse(states)
+        assert np.array_equal(lse, one[0]) or np.max(np.abs(lse - one[0])) < 1e-15
+        assert np.max(np.abs(out - one[1])) < 1e-15
+    lse, out = oracle.merge_lse([empty, empty])
+    assert np.all(np.isneginf(lse)) and np.all(out == 0)
