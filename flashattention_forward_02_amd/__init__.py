@@ -11,6 +11,8 @@ Outputs are allocated with torch on the inputs' device (the library itself never
     O = merge_states(*part, order=[...])              # fold them in the given order
     O, lse = fwd_lse(q, k, v)                         # plus each row's log-sum-exp
     dq, dk, dv = bwd(q, k, v, O, dO, lse)             # gradients, P recomputed from lse
+    plse, po = fwd_split_lse(q, k, v, num_splits=16)  # partial states in the (lse, o / l) form
+    O, lse = merge_lse(plse, po, order=[...])         # combined with weights exp(lse_s - lse)
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ import math
 from . import _native
 from ._native import FaError, FA_F32, FA_BF16, FA_F16  # noqa: F401
 
-__all__ = ["fwd", "fwd_lse", "bwd", "fwd_split", "merge_states", "FaError", "lib_path"]
+__all__ = ["fwd", "fwd_lse", "bwd", "fwd_split", "merge_states", "fwd_split_lse", "merge_lse", "FaError", "lib_path"]
 
 lib_path = _native.LIB_PATH
 
@@ -209,3 +211,42 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal=False, return_delta=False, out
                                  B, H, k.shape[1], Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q.dtype),
                                  _dtype_code(o.dtype), _stream_ptr(q.device)))
     return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
+
+
+def fwd_split_lse(q, k, v, num_splits, scale=None, workspace=None, causal=False):
+    """Split-KV partial states in the (lse, o) form: part_lse [S,B,H,Nq], part_o [S,B,H,Nq,d] (o already divided
+    by the range's own l), fp32. See fa_fwd_split_lse. Grouped heads and ``causal`` as in ``fwd``."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        part_lse = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+        part_o = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    else:
+        part_lse, part_o = workspace
+    _native.check(_native.fa_fwd_split_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), part_lse.data_ptr(),
+                                           part_o.data_ptr(), num_splits, B, H, k.shape[1], Nq, Nk, d, float(scale),
+                                           int(bool(causal)), _dtype_code(q.dtype), _stream_ptr(q.device)))
+    return part_lse, part_o
+
+
+def merge_lse(part_lse, part_o, order=None, out_dtype=None, out=None, return_lse=True):
+    """Combine (lse, o) partial states in ``order``: returns (O [B,H,Nq,d], lse [B,H,Nq]). See fa_merge_lse."""
+    torch = _torch()
+    S, B, H, Nq, d = part_o.shape
+    for t in (part_lse, part_o):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partial states must be contiguous float32")
+    if part_lse.shape != (S, B, H, Nq):
+        raise ValueError("part_lse must be [S, B, H, Nq]")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=part_o.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=part_o.device) if return_lse else None
+    _native.check(_native.fa_merge_lse(part_lse.data_ptr(), part_o.data_ptr(), None if order is None else list(order),
+                                       S, B, H, Nq, d, out.data_ptr(), _dtype_code(out_dtype),
+                                       lse.data_ptr() if lse is not None else None, _stream_ptr(part_o.device)))
+    return (out, lse) if return_lse else out

@@ -14,7 +14,7 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 256
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_fwd_lse", "fa_bwd", "fa_merge_states",
-           "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_fwd_split_lse", "fa_merge_lse", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -41,6 +41,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = I
         L.fa_merge_states.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, P, P]
         L.fa_merge_states.restype = I
+        L.fa_fwd_split_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
+        L.fa_fwd_split_lse.restype = I
+        L.fa_merge_lse.argtypes = [P, P, P, I, I, I, I, I, P, I, P, P]
+        L.fa_merge_lse.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
@@ -95,6 +99,17 @@ def fa_merge_states(part_m, part_l, part_o, order, num_splits, B, H, Nq, d, o, o
         order = (ctypes.c_int * num_splits)(*[int(x) for x in order])
     return lib().fa_merge_states(part_m, part_l, part_o, order, num_splits, B, H, Nq, d, o, out_dtype, m_out, l_out,
                                  stream)
+
+
+def fa_fwd_split_lse(q, k, v, part_lse, part_o, num_splits, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, stream):
+    return lib().fa_fwd_split_lse(q, k, v, part_lse, part_o, num_splits, B, H, H_kv, Nq, Nk, d, scale, causal,
+                                  in_dtype, stream)
+
+
+def fa_merge_lse(part_lse, part_o, order, num_splits, B, H, Nq, d, o, out_dtype, lse_out, stream):
+    if order is not None:
+        order = (ctypes.c_int * num_splits)(*[int(x) for x in order])
+    return lib().fa_merge_lse(part_lse, part_o, order, num_splits, B, H, Nq, d, o, out_dtype, lse_out, stream)
 
 
 def fa_status_string(status: int) -> str:

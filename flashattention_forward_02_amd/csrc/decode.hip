@@ -210,7 +210,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
       store_out<T>(a.o, qrow * D + c, a.out_dtype, o / L);
     } else {
       const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
-      a.part_o[prow * D + c] = o;
+      // (lse, o / l) form: an empty range keeps (-inf, 0)
+      a.part_o[prow * D + c] = (a.split_mode == 2) ? (L > 0.f ? o / L : 0.f) : o;
     }
   }
   if (tid == 0) {
@@ -220,8 +221,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
       if (a.lse_out) a.lse_out[qrow] = m_nat + logf(L);
     } else {
       const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
-      a.part_m[prow] = m_nat;
-      a.part_l[prow] = L;
+      if (a.split_mode == 2) {
+        a.part_m[prow] = (M == -INFINITY) ? -INFINITY : m_nat + logf(L);
+      } else {
+        a.part_m[prow] = m_nat;
+        a.part_l[prow] = L;
+      }
     }
   }
 }

@@ -135,12 +135,13 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
 
 fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const void* v, float* part_m, float* part_l,
                          float* part_o, int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
-                         int causal, fa_dtype in_dtype, void* stream) {
+                         int causal, fa_dtype in_dtype, void* stream, bool lse_form = false) {
   fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
   if (st != FA_OK) return st;
   if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
-  if ((!part_m || !part_l || !part_o) && (size_t)B * H * Nq != 0)
-    return fail(FA_EINVAL, "%s: part_m, part_l and part_o must be non-NULL", fn);
+  if ((!part_m || (!part_l && !lse_form) || !part_o) && (size_t)B * H * Nq != 0)
+    return fail(FA_EINVAL, lse_form ? "%s: part_lse and part_o must be non-NULL"
+                                    : "%s: part_m, part_l and part_o must be non-NULL", fn);
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS || num_splits > Nk)
     return fail(FA_EINVAL, "%s: num_splits=%d must be in [1, min(Nk=%d, %d)]", fn, num_splits, Nk, FA_MAX_SPLITS);
   if (!aligned16(part_o) || !aligned4(part_m) || !aligned4(part_l))
@@ -152,13 +153,57 @@ fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const voi
   a.part_l = part_l;
   a.part_o = part_o;
   a.num_splits = num_splits;
-  a.split_mode = 1;
+  a.split_mode = lse_form ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
   return launched(fn, e);
+}
+
+// Shared by fa_merge_states ((m, l, o) parts) and fa_merge_lse ((lse, o) parts: part_l unused).
+fa_status merge_impl(const char* fn, bool lse_form, const float* part_m, const float* part_l, const float* part_o,
+                     const int* order, int num_splits, int B, int H, int Nq, int d, void* o, fa_dtype out_dtype,
+                     float* m_out, float* l_out, float* lse_out, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0) return fail(FA_EINVAL, "%s: B=%d, H=%d, Nq=%d must be >= 0", fn, B, H, Nq);
+  if ((!part_m || (!part_l && !lse_form) || !part_o || !o) && (size_t)B * H * Nq != 0)
+    return fail(FA_EINVAL, lse_form ? "%s: part_lse, part_o and o must be non-NULL"
+                                    : "%s: part_m, part_l, part_o and o must be non-NULL", fn);
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS)
+    return fail(FA_EINVAL, "%s: num_splits=%d must be in [1, %d]", fn, num_splits, FA_MAX_SPLITS);
+  if (!valid_dtype(out_dtype)) return fail(FA_EINVAL, "%s: out_dtype=%d is not a fa_dtype", fn, (int)out_dtype);
+  if (d <= 0) return fail(FA_EINVAL, "%s: d=%d must be > 0", fn, d);
+  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "%s: head dimension d=%d (supported: 64, 128)", fn, d);
+  if (!aligned16(part_o) || !aligned16(o) || !aligned4(part_m) || !aligned4(part_l) || !aligned4(m_out) ||
+      !aligned4(l_out) || !aligned4(lse_out))
+    return fail(FA_EINVAL, "%s: part_o and o must be 16-byte aligned, the rest 4-byte aligned", fn);
+
+  fa::MergeArgs a;
+  memset(&a, 0, sizeof(a));
+  bool seen[FA_MAX_SPLITS] = {false};
+  for (int i = 0; i < num_splits; ++i) {
+    const int s = order ? order[i] : i;
+    if (s < 0 || s >= num_splits || seen[s])
+      return fail(FA_EINVAL, "%s: order is not a permutation of 0..%d (entry %d = %d)", fn, num_splits - 1, i, s);
+    seen[s] = true;
+    a.order[i] = (unsigned short)s;
+  }
+  const long long rows = (long long)B * H * Nq;
+  if (rows == 0) return FA_OK;
+  if (rows > 0x7fffffffLL) return fail(FA_EINVAL, "%s: B*H*Nq=%lld exceeds 2^31-1", fn, rows);
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_o = part_o;
+  a.o = o;
+  a.m_out = m_out;
+  a.l_out = l_out;
+  a.lse_out = lse_out;
+  a.lse_format = lse_form ? 1 : 0;
+  a.S = num_splits;
+  a.rows = (int)rows;
+  a.out_dtype = out_dtype;
+  return launched(fn, fa::launch_merge(a, d, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -266,41 +311,23 @@ fa_status fa_merge_states(const float* part_m, const float* part_l, const float*
                           int num_splits, int B, int H, int Nq, int d, void* o, fa_dtype out_dtype, float* m_out,
                           float* l_out, void* stream) {
   g_last_error[0] = 0;
-  if (B < 0 || H < 0 || Nq < 0) return fail(FA_EINVAL, "fa_merge_states: B=%d, H=%d, Nq=%d must be >= 0", B, H, Nq);
-  if ((!part_m || !part_l || !part_o || !o) && (size_t)B * H * Nq != 0)
-    return fail(FA_EINVAL, "fa_merge_states: part_m, part_l, part_o and o must be non-NULL");
-  if (num_splits < 1 || num_splits > FA_MAX_SPLITS)
-    return fail(FA_EINVAL, "fa_merge_states: num_splits=%d must be in [1, %d]", num_splits, FA_MAX_SPLITS);
-  if (!valid_dtype(out_dtype)) return fail(FA_EINVAL, "fa_merge_states: out_dtype=%d is not a fa_dtype", (int)out_dtype);
-  if (d <= 0) return fail(FA_EINVAL, "fa_merge_states: d=%d must be > 0", d);
-  if (d != 64 && d != 128) return fail(FA_EUNSUPPORTED, "fa_merge_states: head dimension d=%d (supported: 64, 128)", d);
-  if (!aligned16(part_o) || !aligned16(o) || !aligned4(part_m) || !aligned4(part_l) || !aligned4(m_out) ||
-      !aligned4(l_out))
-    return fail(FA_EINVAL, "fa_merge_states: part_o and o must be 16-byte aligned, the rest 4-byte aligned");
+  return merge_impl("fa_merge_states", false, part_m, part_l, part_o, order, num_splits, B, H, Nq, d, o, out_dtype,
+                    m_out, l_out, nullptr, stream);
+}
 
-  fa::MergeArgs a;
-  memset(&a, 0, sizeof(a));
-  bool seen[FA_MAX_SPLITS] = {false};
-  for (int i = 0; i < num_splits; ++i) {
-    const int s = order ? order[i] : i;
-    if (s < 0 || s >= num_splits || seen[s])
-      return fail(FA_EINVAL, "fa_merge_states: order is not a permutation of 0..%d (entry %d = %d)", num_splits - 1, i, s);
-    seen[s] = true;
-    a.order[i] = (unsigned short)s;
-  }
-  const long long rows = (long long)B * H * Nq;
-  if (rows == 0) return FA_OK;
-  if (rows > 0x7fffffffLL) return fail(FA_EINVAL, "fa_merge_states: B*H*Nq=%lld exceeds 2^31-1", rows);
-  a.part_m = part_m;
-  a.part_l = part_l;
-  a.part_o = part_o;
-  a.o = o;
-  a.m_out = m_out;
-  a.l_out = l_out;
-  a.S = num_splits;
-  a.rows = (int)rows;
-  a.out_dtype = out_dtype;
-  return launched("fa_merge_states", fa::launch_merge(a, d, static_cast<hipStream_t>(stream)));
+fa_status fa_fwd_split_lse(const void* q, const void* k, const void* v, float* part_lse, float* part_o,
+                           int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                           fa_dtype in_dtype, void* stream) {
+  g_last_error[0] = 0;
+  return fwd_split_impl("fa_fwd_split_lse", q, k, v, part_lse, nullptr, part_o, num_splits, B, H, H_kv, Nq, Nk, d,
+                        scale, causal, in_dtype, stream, true);
+}
+
+fa_status fa_merge_lse(const float* part_lse, const float* part_o, const int* order, int num_splits, int B, int H,
+                       int Nq, int d, void* o, fa_dtype out_dtype, float* lse_out, void* stream) {
+  g_last_error[0] = 0;
+  return merge_impl("fa_merge_lse", true, part_lse, nullptr, part_o, order, num_splits, B, H, Nq, d, o, out_dtype,
+                    nullptr, nullptr, lse_out, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -27,7 +27,7 @@ struct FwdArgs {
   int causal;       // 1: query row i sees keys j <= i + causal_off only
   int causal_off;   // Nk - Nq
   int num_splits;   // 1 in full mode
-  int split_mode;   // 0: final output, 1: partial states
+  int split_mode;   // 0: final output, 1: partial states (m, l, o), 2: partial states (lse, o / l)
   int out_dtype;    // Dtype of o (full mode)
   float scale;      // softmax scale applied to q.k (natural-log units)
   float scale_log2e;  // scale * log2(e): scores in base-2 units for exp2
@@ -45,6 +45,8 @@ struct MergeArgs {
   float* l_out;
   int S, rows;      // rows = B * H * Nq
   int out_dtype;
+  int lse_format;   // 1: parts are (lse, normalised o) in part_m / part_o; lse_out receives the total
+  float* lse_out;
   unsigned short order[kMaxSplits];
 };
 

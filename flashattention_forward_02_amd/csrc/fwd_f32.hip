@@ -162,14 +162,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
   } else {
     const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;
     float* P = a.part_o + prow * D + col0;
+    // (lse, o / l) form: a row with no key in this range keeps (-inf, 0)
+    const float w = (a.split_mode == 2) ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
 #pragma unroll
     for (int c = 0; c < 32; c += 4) {
-      f32x4_t x = {acc[c], acc[c + 1], acc[c + 2], acc[c + 3]};
+      f32x4_t x = {acc[c] * w, acc[c + 1] * w, acc[c + 2] * w, acc[c + 3] * w};
       *reinterpret_cast<f32x4_t*>(P + c) = x;
     }
     if (col0 == 0) {
-      a.part_m[prow] = m;
-      a.part_l[prow] = l;
+      if (a.split_mode == 2) {
+        a.part_m[prow] = (m == -INFINITY) ? -INFINITY : m + logf(l);
+      } else {
+        a.part_m[prow] = m;
+        a.part_l[prow] = l;
+      }
     }
   }
 }

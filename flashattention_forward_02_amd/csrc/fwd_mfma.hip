@@ -646,20 +646,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
       }
     } else if constexpr (!FAST) {
       // A row that saw no key of this range (causal mask) keeps the empty state (-inf, 0, 0).
+      // In the (lse, o / l) form the empty state is (-inf, 0).
       const bool empty = st.mraw[nb] == -INFINITY;
       const float to_true = empty ? 0.f : __builtin_amdgcn_exp2f(st.m2ref[nb] - st.mraw[nb] * c2);
+      const bool lse_form = a.split_mode == 2;
+      const float w = lse_form ? (empty ? 0.f : 1.f / st.lsum[nb]) : to_true;
       const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int dd = db * 32 + 8 * g4 + 4 * hf;
-          store4(a.part_o, prow * D + dd, kF32, acc[nb][db][4 * g4] * to_true, acc[nb][db][4 * g4 + 1] * to_true,
-                 acc[nb][db][4 * g4 + 2] * to_true, acc[nb][db][4 * g4 + 3] * to_true);
+          store4(a.part_o, prow * D + dd, kF32, acc[nb][db][4 * g4] * w, acc[nb][db][4 * g4 + 1] * w,
+                 acc[nb][db][4 * g4 + 2] * w, acc[nb][db][4 * g4 + 3] * w);
         }
       if (hf == 0) {
-        a.part_m[prow] = empty ? -INFINITY : a.scale * st.mraw[nb];
-        a.part_l[prow] = st.lsum[nb] * to_true;
+        if (lse_form) {
+          a.part_m[prow] = empty ? -INFINITY : a.scale * st.mraw[nb] + logf(st.lsum[nb] * to_true);
+        } else {
+          a.part_m[prow] = empty ? -INFINITY : a.scale * st.mraw[nb];
+          a.part_l[prow] = st.lsum[nb] * to_true;
+        }
       }
     }
   }

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 #define FA_MAX_SPLITS 256
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
@@ -183,6 +183,32 @@ fa_status fa_fwd_split_ext(const void* q, const void* k, const void* v,
 fa_status fa_merge_states(const float* part_m, const float* part_l, const float* part_o,
                           const int* order, int num_splits, int B, int H, int Nq, int d,
                           void* o, fa_dtype out_dtype, float* m_out, float* l_out, void* stream);
+
+/*
+ * fa_fwd_split_lse -- split-KV partial states in the (lse, o) form.
+ *
+ * "CS349E 第 11 讲 01_online_softmax.py" (its note after demo 2): flash-decoding stores, per key
+ * range s, the output already divided by that range's own l, o_s / l_s, and lse_s = m_s + ln(l_s)
+ * -- one value fewer than (m, l, o) -- and combines the ranges with weights exp(lse_s - lse).
+ *   part_lse [S,B,H,Nq] fp32   lse_s (-inf for a range holding no key the row may see)
+ *   part_o   [S,B,H,Nq,d] fp32 o_s / l_s (0 for such a range)
+ * Partition, H_kv, causal, dtypes and errors as in fa_fwd_split_ext.
+ */
+fa_status fa_fwd_split_lse(const void* q, const void* k, const void* v, float* part_lse, float* part_o,
+                           int num_splits, int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+                           int causal, fa_dtype in_dtype, void* stream);
+
+/*
+ * fa_merge_lse -- combine (lse, o) partial states into the attention output.
+ *
+ * lse = ln(sum_s exp(lse_s)) (computed as max_s lse_s + ln sum_s exp(lse_s - max)), then
+ * O = sum_s exp(lse_s - lse) o_s, both sums taken in the order given by `order` (a host
+ * permutation of 0..num_splits-1; NULL = ascending). Ranges with lse_s = -inf weigh 0; a row whose
+ * ranges are all empty gets O = 0 and lse = -inf. o [B,H,Nq,d] in out_dtype; lse_out [B,H,Nq] fp32
+ * (NULL to skip) receives lse, the row log-sum-exp of the whole key range.
+ */
+fa_status fa_merge_lse(const float* part_lse, const float* part_o, const int* order, int num_splits,
+                       int B, int H, int Nq, int d, void* o, fa_dtype out_dtype, float* lse_out, void* stream);
 
 /* Name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_string(int status);

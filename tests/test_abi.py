@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert n.fa_abi_version() == 3
+    assert n.fa_abi_version() == 4
     assert [n.fa_status_string(s) for s in range(4)] == ["FA_OK", "FA_EINVAL", "FA_EUNSUPPORTED", "FA_EHIP"]
     assert n.fa_status_string(99) == "FA_UNKNOWN_STATUS"
 
@@ -246,3 +246,45 @@ def test_fa_bwd_empty_batch_is_ok_without_device():
     assert bwd(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, delta=None, dq=None, dk=None,
                dv=None) == n.FA_OK
     assert n.fa_last_error() == ""
+
+
+def split_lse(**kw):
+    a = dict(q=P, k=P, v=P, part_lse=P * 2, part_o=P * 3, num_splits=2, B=1, H=2, H_kv=2, Nq=8, Nk=8, d=64,
+             scale=0.125, causal=0, in_dtype=n.FA_BF16, stream=None)
+    a.update(kw)
+    return n.fa_fwd_split_lse(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(part_lse=None), n.FA_EINVAL, "part_lse and part_o"),
+    (dict(part_o=None), n.FA_EINVAL, "part_lse and part_o"),
+    (dict(num_splits=0), n.FA_EINVAL, "num_splits"),
+    (dict(num_splits=9), n.FA_EINVAL, "num_splits"),
+    (dict(part_o=P * 3 + 4), n.FA_EINVAL, "aligned"),
+    (dict(causal=1, Nq=9), n.FA_EINVAL, "Nq <= Nk"),
+])
+def test_fa_fwd_split_lse_rejects(kw, status, msg):
+    assert split_lse(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def merge_lse(**kw):
+    a = dict(part_lse=P, part_o=P * 2, order=None, num_splits=3, B=1, H=2, Nq=8, d=64, o=P * 3, out_dtype=n.FA_F32,
+             lse_out=None, stream=None)
+    a.update(kw)
+    return n.fa_merge_lse(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(part_lse=None), n.FA_EINVAL, "non-NULL"),
+    (dict(o=None), n.FA_EINVAL, "non-NULL"),
+    (dict(num_splits=0), n.FA_EINVAL, "num_splits"),
+    (dict(order=[0, 0, 1]), n.FA_EINVAL, "permutation"),
+    (dict(order=[0, 1, 3]), n.FA_EINVAL, "permutation"),
+    (dict(d=96), n.FA_EUNSUPPORTED, "d=96"),
+    (dict(lse_out=P * 4 + 2), n.FA_EINVAL, "aligned"),
+    (dict(out_dtype=9), n.FA_EINVAL, "out_dtype"),
+])
+def test_fa_merge_lse_rejects(kw, status, msg):
+    assert merge_lse(**kw) == status
+    assert msg in n.fa_last_error()
