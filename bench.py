@@ -1,10 +1,11 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload headline|long_seq|causal|decode|gqa_decode|bwd] [--no-cpu]
+                    [--workload headline|headline_f16|long_seq|causal|decode|decode_lse|gqa_decode|bwd]
+                    [--no-cpu]
 
-A step is one forward over the whole batch (headline, long_seq, causal), one split + merge pair
-(decode, gqa_decode), or one backward call over the whole batch (bwd: dQ, dK, dV from the stored
+A step is one forward over the whole batch (headline, headline_f16, long_seq, causal), one split +
+merge pair (decode, gqa_decode; decode_lse with the states in the (lse, o) form), or one backward call over the whole batch (bwd: dQ, dK, dV from the stored
 log-sum-exp; the forward that produces O and it runs once before the timed region). Inputs are generated and resident in HBM before the timed region. Prints ONE
 JSON line. The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per
 step); the causal workload counts 4*d flops per visible (query, key) pair.
@@ -32,7 +33,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="headline",
-                   choices=["headline", "long_seq", "causal", "decode", "gqa_decode", "bwd"])
+                   choices=["headline", "headline_f16", "long_seq", "causal", "decode", "decode_lse", "gqa_decode",
+                            "bwd"])
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
@@ -133,9 +135,11 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16,
-          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16, "bwd": si.BWD_BF16}[args.workload]
+          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16, "bwd": si.BWD_BF16,
+          "headline_f16": si.HEADLINE_F16, "decode_lse": si.DECODE_BF16}[args.workload]
     is_bwd = args.workload == "bwd"
-    is_decode = args.workload in ("decode", "gqa_decode")
+    is_decode = args.workload in ("decode", "gqa_decode", "decode_lse")
+    lse_form = args.workload == "decode_lse"
 
     if is_decode:
         q, k, v = si.decode_inputs_device(wl, dev)
@@ -167,10 +171,16 @@ def main():
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            fa.fwd_split(q, k, v, S, scale=wl.scale, workspace=(pm, pl, po))
+            if lse_form:
+                fa.fwd_split_lse(q, k, v, S, scale=wl.scale, workspace=(pm, po))
+            else:
+                fa.fwd_split(q, k, v, S, scale=wl.scale, workspace=(pm, pl, po))
             if ev is not None:
                 ev[1].record(stream)
-            fa.merge_states(pm, pl, po, order=order, out=o)
+            if lse_form:
+                fa.merge_lse(pm, po, order=order, out=o, return_lse=False)
+            else:
+                fa.merge_states(pm, pl, po, order=order, out=o)
     elif is_bwd:
         o, lse = fa.fwd_lse(q, k, v, scale=wl.scale)
         grads = (torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32),
@@ -224,9 +234,11 @@ def main():
     if is_decode:
         split_ms = avg_launch_ms
         kv_bytes = 2.0 * wl.B * wl.kv_heads * wl.Nk * wl.d * 2
-        alg_bytes = kv_bytes + wl.B * wl.H * wl.d * 2 + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4
-        step_bytes = alg_bytes + wl.num_splits * wl.B * wl.H * (wl.d + 2) * 4 + wl.B * wl.H * wl.d * 4
-        result.update({"metric": "split-KV decode HBM GB/s (K+V bytes / step time)", "unit": "GB/s",
+        state_vals = wl.d + (1 if lse_form else 2)           # (lse, o) or (m, l, o) per row and range
+        alg_bytes = kv_bytes + wl.B * wl.H * wl.d * 2 + wl.num_splits * wl.B * wl.H * state_vals * 4
+        step_bytes = alg_bytes + wl.num_splits * wl.B * wl.H * state_vals * 4 + wl.B * wl.H * wl.d * 4
+        result.update({"metric": "split-KV decode HBM GB/s (K+V bytes / step time)" +
+                                 (", partial states in the (lse, o) form" if lse_form else ""), "unit": "GB/s",
                        "value": kv_bytes / (ms_per_step * 1e-3) / 1e9,
                        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "H_kv": wl.kv_heads, "Nq": wl.Nq,
                                   "Nk": wl.Nk, "d": wl.d, "num_splits": wl.num_splits,
@@ -235,6 +247,8 @@ def main():
         result["roofline"] = {"bound": "hbm", "kernel": "decode_kernel (split)", "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                               **launch_stats, "traffic": traffic_for(args.workload, source_hash("decode.hip"))}
+        if wl.dtype != "bf16":
+            result["dtype"] = wl.dtype
         result["step_bytes"] = step_bytes
     elif is_bwd:
         flops = 10.0 * wl.B * wl.H * wl.Nq * wl.Nk * wl.d
@@ -253,6 +267,9 @@ def main():
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         if args.workload == "long_seq":
             result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=16384,d=128 bf16, K x3; % of MFMA peak"
+        if args.workload == "headline_f16":
+            result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 fp16; % of MFMA peak"
+            result["dtype"] = "fp16"
         if args.workload == "causal":
             result["metric"] = ("FA fwd causal TFLOP/s (4*d per visible query-key pair, B*H*N(N+1)/2 pairs) "
                                 "at N=4096,d=64 bf16; % of MFMA peak")

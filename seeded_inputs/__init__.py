@@ -180,6 +180,8 @@ HEADLINE_BF16 = Workload("headline B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096
 LONG_SEQ_BF16 = Workload("long_seq B=1 H=32 N=16384 d=128 bf16 Kx3", 1, 32, 16384, 16384, 128, "bf16", 4,
                          k_mult=3.0)
 CAUSAL_BF16 = Workload("causal B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096, 64, "bf16", 3, causal=True)
+# The headline shape in fp16 (the same draws rounded to fp16).
+HEADLINE_F16 = Workload("headline_f16 B=4 H=16 N=4096 d=64 fp16", 4, 16, 4096, 4096, 64, "f16", 3)
 # The backward pass on the headline inputs; dL/dO is tensor 3 of the same per-head draws.
 BWD_BF16 = Workload("backward B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 64, "bf16", 3)
 GQA_DECODE_BF16 = Workload("gqa_decode B=16 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 6,
