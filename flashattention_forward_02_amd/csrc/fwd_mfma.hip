@@ -66,10 +66,10 @@ constexpr int kWaves = 8;                    // two groups of four, one wave of 
 constexpr int kThreads = kWaves * 64;
 constexpr int kBC = 64;                      // keys per tile
 
-template <int D, typename T>
+template <int D, typename T, int NB_ = (D <= 64) ? 2 : 1>
 struct Cfg {
   typedef typename Mma<T>::v8 v8;
-  static constexpr int NB = (D <= 64) ? 2 : 1;     // 32-query MFMA column blocks per wave
+  static constexpr int NB = NB_;                   // 32-query MFMA column blocks per wave
   static constexpr int BR = kWaves * NB * 32;      // query rows per workgroup
   static constexpr int KS = D / 16;                // 16-wide k steps of S^T = K Q^T
   static constexpr int DB = D / 32;                // 32-row blocks of O^T
@@ -102,7 +102,13 @@ __device__ __forceinline__ void load_tile2(const T* __restrict__ X, T* lx, int k
   if (key0 + kBC <= kend) {
     const char* g = reinterpret_cast<const char*>(X + (size_t)key0 * D);
 #pragma unroll
-    for (int i = 0; i < C::LPW; ++i) global_to_lds16(g + off[i], &lx[(gw * C::CPW + i * 64) * 8]);
+    for (int i = 0; i < C::LPW; ++i) {
+      // an opaque copy keeps the offset 32-bit: the compiler would otherwise hoist 64-bit
+      // per-lane addresses out of the tile loop and spill them where registers are short
+      unsigned o = off[i];
+      asm volatile("" : "+v"(o));
+      global_to_lds16(g + o, &lx[(gw * C::CPW + i * 64) * 8]);
+    }
     return;
   }
 #pragma unroll
@@ -130,10 +136,10 @@ __device__ __forceinline__ void load_offsets(int gw, int lane, unsigned (&off)[C
 }
 
 // S^T = K Q^T for one tile: rows = 64 keys (two 32-blocks), columns = this wave's queries.
-template <int D, typename T>
-__device__ __forceinline__ void s_tile(const T* __restrict__ lk, const typename Cfg<D, T>::v8 (&qf)[Cfg<D, T>::NB][Cfg<D, T>::KS],
-                                       f32x16_t (&s)[Cfg<D, T>::NB][2], int lane) {
-  typedef Cfg<D, T> C;
+template <int D, typename T, int NB>
+__device__ __forceinline__ void s_tile(const T* __restrict__ lk, const typename Cfg<D, T, NB>::v8 (&qf)[NB][Cfg<D, T, NB>::KS],
+                                       f32x16_t (&s)[NB][2], int lane) {
+  typedef Cfg<D, T, NB> C;
   typedef typename C::v8 v8;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
@@ -157,10 +163,10 @@ __device__ __forceinline__ void s_tile(const T* __restrict__ lk, const typename 
 }
 
 // O^T += V^T P^T for one tile: 16 keys per MFMA step, V^T read transposed from row-major LDS.
-template <int D, typename T>
-__device__ __forceinline__ void pv_tile(const T* __restrict__ lv, const typename Cfg<D, T>::v8 (&pf)[Cfg<D, T>::NB][4],
-                                        f32x16_t (&acc)[Cfg<D, T>::NB][Cfg<D, T>::DB], int lane) {
-  typedef Cfg<D, T> C;
+template <int D, typename T, int NB>
+__device__ __forceinline__ void pv_tile(const T* __restrict__ lv, const typename Cfg<D, T, NB>::v8 (&pf)[NB][4],
+                                        f32x16_t (&acc)[NB][Cfg<D, T, NB>::DB], int lane) {
+  typedef Cfg<D, T, NB> C;
   typedef typename C::v8 v8;
   const int hf = lane >> 5;
   const int tj = lane & 15;
@@ -216,10 +222,10 @@ __device__ __forceinline__ void stage_v(const T* __restrict__ lv, T* vfrag, int 
 }
 
 // O^T += V^T P^T for one tile from staged fragments: one 16-byte LDS read per MFMA A operand.
-template <int D, typename T>
-__device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typename Cfg<D, T>::v8 (&pf)[Cfg<D, T>::NB][4],
-                                          f32x16_t (&acc)[Cfg<D, T>::NB][Cfg<D, T>::DB], int lane) {
-  typedef Cfg<D, T> C;
+template <int D, typename T, int NB>
+__device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typename Cfg<D, T, NB>::v8 (&pf)[NB][4],
+                                          f32x16_t (&acc)[NB][Cfg<D, T, NB>::DB], int lane) {
+  typedef Cfg<D, T, NB> C;
   typedef typename C::v8 v8;
 #pragma unroll
   for (int g = 0; g < kBC / 16; ++g)
@@ -239,16 +245,20 @@ __device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typ
 // Exponentials of one block's scores: p = 2^(s c2 - ref), 0 for masked (-inf) scores; returns
 // the row sum. At d = 64 the P operands are also rounded here (measured 1.5 % faster there; at
 // d = 128 rounding after the softmax update measured 2 % faster).
+// Key index (within the tile, minus 4 hf) of value i = 16 kb + r of a 64-key block: key
+// 32 kb + 8 (r / 4) + 4 hf + r % 4 is masked when tail_key(i) >= limh = lim - 4 hf.
+__host__ __device__ constexpr int tail_key(int i) { return 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3); }
+
 template <int D, typename T, bool TAIL>
 __device__ __forceinline__ float exps_block(const f32x16_t (&s)[2], float ref, float c2, float (&p)[32],
-                                           typename Cfg<D, T>::v8 (&pf)[4]) {
+                                           typename Cfg<D, T>::v8 (&pf)[4], int limh) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) p[i] = __builtin_fmaf(s[i >> 4][i & 15], c2, -ref);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     float x = __builtin_amdgcn_exp2f(p[i]);
     if constexpr (TAIL) {
-      if (s[i >> 4][i & 15] == -INFINITY) x = 0.f;
+      if (tail_key(i) >= limh) x = 0.f;
     }
     p[i] = x;
   }
@@ -262,10 +272,14 @@ __device__ __forceinline__ float exps_block(const f32x16_t (&s)[2], float ref, f
   return xhalf_sum((r4[0] + r4[1]) + (r4[2] + r4[3]));
 }
 
-__device__ __forceinline__ float max_block(const f32x16_t (&s)[2]) {
-  float mx = s[0][0];
+template <bool TAIL>
+__device__ __forceinline__ float max_block(const f32x16_t (&s)[2], int limh) {
+  float mx = -INFINITY;
 #pragma unroll
-  for (int i = 1; i < 32; ++i) mx = fmaxf(mx, s[i >> 4][i & 15]);
+  for (int i = 0; i < 32; ++i) {
+    if (TAIL && tail_key(i) >= limh) continue;
+    mx = fmaxf(mx, s[i >> 4][i & 15]);
+  }
   return xhalf_max(mx);
 }
 
@@ -296,26 +310,27 @@ __device__ __forceinline__ bool move_ref(bool need, float target, bool first, fl
 // accumulator), writes P as PV operands and adds its row sum to l.
 //   FAST = false: exact running max, reference moves when the tile max exceeds it by > tau.
 //   FAST = true:  no running max; reference moves when the tile's row sum leaves [0, 2^tau].
+// TAIL: keys with tail_key >= limh (per lane) are masked (p = 0, and no part of the maximum).
 template <int D, typename T, bool FAST, bool TAIL>
 __device__ __forceinline__ void softmax_block(const f32x16_t (&s)[2], float& mraw, float& m2ref, float& lsum,
                                               typename Cfg<D, T>::v8 (&pf)[4], f32x16_t (&acc)[Cfg<D, T>::DB],
-                                              bool first, float c2, float tau, float bound) {
+                                              bool first, float c2, float tau, float bound, int limh = 0) {
   float p[32];
   float rs;
   if constexpr (FAST) {
-    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf);
+    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf, limh);
     const bool trig = first || !(rs <= bound);
     if (__ballot(trig)) {
-      const float mx2 = max_block(s) * c2;
+      const float mx2 = max_block<TAIL>(s, limh) * c2;
       if (move_ref<D>(trig, first ? mx2 : fmaxf(m2ref, mx2), first, m2ref, lsum, acc))
-        rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf);
+        rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf, limh);
     }
   } else {
-    const float mx = max_block(s);
+    const float mx = max_block<TAIL>(s, limh);
     mraw = fmaxf(mraw, mx);
     const float mx2 = mx == -INFINITY ? -INFINITY : mx * c2;  // a wholly masked tile (scale may be 0)
     move_ref<D>(first || (mx2 > m2ref + tau), mx2, first, m2ref, lsum, acc);
-    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf);
+    rs = exps_block<D, T, TAIL>(s, m2ref, c2, p, pf, limh);
   }
   lsum += rs;
   if constexpr (D != 64) {
@@ -433,10 +448,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
   __shared__ __attribute__((aligned(16))) T lds_vf[STAGE ? 2 : 1][STAGE ? C::ELEMS : 8];  // staged fragments
 
   // ---- work item: (query tile, split, h, b) ----
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  // Under the causal mask later query tiles see more keys: hand them out first.
-  const int qt = CAUSAL ? n_qtiles - 1 - wg % n_qtiles : wg % n_qtiles;
-  int rest = wg / n_qtiles;
+  // Without the mask: the query tile varies fastest, and the XCD remap keeps a head's tiles on one
+  // XCD (one L2). Under the causal mask later query tiles see more keys and are handed out first
+  // (longest first: the hardware dispatches blocks in order as compute units free up); the query
+  // tile varies slowest, and with a multiple of 8 (split, head) units a head's tiles all land on
+  // the XCD that takes block index mod 8.
+  int qt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_qtiles;
+    qt = n_qtiles - 1 - (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    qt = wg % n_qtiles;
+    rest = wg / n_qtiles;
+  }
   const int split = rest % a.num_splits;
   rest /= a.num_splits;
   const int h = rest % a.H;
@@ -512,6 +538,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
       for (int r = 0; r < 16; ++r) acc[nb][db][r] = 0.f;
   }
 
+  // Causal: no row of this wave sees a key of tile t (wave-uniform; once true, true for every
+  // later tile).
+  const int wave_row0 = __builtin_amdgcn_readfirstlane(qrow0);
+  auto wave_masked = [&](int t) -> bool {
+    if constexpr (CAUSAL) return wave_row0 + NB * 32 + a.causal_off <= kbeg + t * kBC;
+    else return false;
+  };
+
   // ---- the two phases of one tile ----
   // Loads (group A only; global -> LDS, asynchronous). Staged: K(t+1) and V(t+1) start at the top
   // of the MFMA phase of tile t. Otherwise K(t+1) and V(t) start at the top of the VALU phase of
@@ -525,18 +559,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
         load_tile2<D, T, true>(K, lds_k[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane, koff);
         load_tile2<D, T, false>(V, lds_v[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane, voff);
       }
-      if (do_pv && do_s) {
-        const unsigned vo = ((t - 1) & 1) * (unsigned)(C::ELEMS * sizeof(T));
-        const unsigned ko = (t & 1) * (unsigned)(C::ELEMS * sizeof(T));
-        const unsigned kaddr[4] = {kaddr0[0] + ko, kaddr0[1] + ko, kaddr0[2] + ko, kaddr0[3] + ko};
-        mfma_phase_d64<T>(vaddr0 + vo, kaddr, pf, qf, acc, s);
+      if constexpr (NB == 2) {
+        if (do_pv && do_s) {
+          const unsigned vo = ((t - 1) & 1) * (unsigned)(C::ELEMS * sizeof(T));
+          const unsigned ko = (t & 1) * (unsigned)(C::ELEMS * sizeof(T));
+          const unsigned kaddr[4] = {kaddr0[0] + ko, kaddr0[1] + ko, kaddr0[2] + ko, kaddr0[3] + ko};
+          mfma_phase_d64<T>(vaddr0 + vo, kaddr, pf, qf, acc, s);
+        } else if (do_pv) {
+          pv_staged<D, T, NB>(lds_vf[(t - 1) & 1], pf, acc, lane);
+        }
       } else if (do_pv) {
-        pv_staged<D, T>(lds_vf[(t - 1) & 1], pf, acc, lane);
+        pv_staged<D, T, NB>(lds_vf[(t - 1) & 1], pf, acc, lane);
       }
     } else {
-      if (do_pv) pv_tile<D, T>(lds_v[(t - 1) & 1], pf, acc, lane);
+      if (do_pv) pv_tile<D, T, NB>(lds_v[(t - 1) & 1], pf, acc, lane);
     }
-    if (do_s && !(STAGE && do_pv)) s_tile<D, T>(lds_k[t & 1], qf, s, lane);
+    if (do_s && !(STAGE && NB == 2 && do_pv)) s_tile<D, T, NB>(lds_k[t & 1], qf, s, lane);
     if constexpr (D == 128) {
       if (do_pv && do_s) mfma_phase_order_d128<2, 0>();
     }
@@ -561,27 +599,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
     if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  // Masked tiles: keys past the range end (a ragged last tile) or past the row's last visible
-  // key (causal) get score -inf.
+  // Masked tiles: a row sees the tile's keys below lim (the range end: a ragged last tile; the
+  // row's last visible key + 1: causal), and the keys at or past it are masked one by one. Under
+  // the causal mask a tile of which no row of the wave sees any key (a wave-uniform test on the
+  // wave's last row) takes a short path instead: P = 0 and the state is unchanged. The first tile
+  // always takes the per-key path, which sets up the state.
   auto phase_valu_masked = [&](int t, bool first) {
     valu_prologue(t);
     const int k0 = kbeg + t * kBC;
+    if (CAUSAL && !first && wave_masked(t)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int lim = kend - k0;
-      if constexpr (CAUSAL) lim = min(lim, qrow0 + nb * 32 + l32 + a.causal_off + 1 - k0);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= lim) s[nb][kb][r] = -INFINITY;
-        }
+          for (int i = 0; i < 8; ++i) pf[nb][g][i] = (T)0.f;
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        int lim = kend - k0;
+        if constexpr (CAUSAL) lim = min(lim, wave_row0 + nb * 32 + l32 + a.causal_off + 1 - k0);
+        softmax_block<D, T, FAST, true>(s[nb], st.mraw[nb], st.m2ref[nb], st.lsum[nb], pf[nb], acc[nb], first, c2,
+                                        tau, bound, lim - 4 * hf);
+      }
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      softmax_block<D, T, FAST, true>(s[nb], st.mraw[nb], st.m2ref[nb], st.lsum[nb], pf[nb], acc[nb], first, c2, tau,
-                                      bound);
     if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -674,8 +715,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
 
 template <int D, typename T>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
-  typedef Cfg<D, T> C;
-  const int n_qtiles = (a.Nq + C::BR - 1) / C::BR;
+  const int n_qtiles = (a.Nq + Cfg<D, T>::BR - 1) / Cfg<D, T>::BR;
   const long long nwg = (long long)n_qtiles * a.num_splits * a.H * a.B;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
