@@ -1,14 +1,16 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload headline|headline_f16|long_seq|causal|decode|decode_lse|gqa_decode|bwd]
+                    [--workload headline|headline_f16|long_seq|causal|decode|decode_lse|gqa_decode|bwd|bwd_causal]
                     [--no-cpu]
 
 A step is one forward over the whole batch (headline, headline_f16, long_seq, causal), one split +
-merge pair (decode, gqa_decode; decode_lse with the states in the (lse, o) form), or one backward call over the whole batch (bwd: dQ, dK, dV from the stored
-log-sum-exp; the forward that produces O and it runs once before the timed region). Inputs are generated and resident in HBM before the timed region. Prints ONE
-JSON line. The default workload is B=4, H=16, N=4096, d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per
-step); the causal workload counts 4*d flops per visible (query, key) pair.
+merge pair (decode, gqa_decode; decode_lse with the states in the (lse, o) form), or one backward
+call over the whole batch (bwd, bwd_causal: dQ, dK, dV from the stored log-sum-exp; the forward
+that produces O and it runs once before the timed region). Inputs are generated and resident in
+HBM before the timed region. Prints ONE JSON line. The default workload is B=4, H=16, N=4096,
+d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per step); the causal workloads count 4*d (forward) or
+10*d (backward) flops per visible (query, key) pair.
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="headline",
                    choices=["headline", "headline_f16", "long_seq", "causal", "decode", "decode_lse", "gqa_decode",
-                            "bwd"])
+                            "bwd", "bwd_causal"])
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
@@ -105,7 +107,8 @@ def cpu_baseline_bwd(w, q, k, v, do, grads, max_heads):
     done = 0
     for (b, h) in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.attention_backward_fp64(*(si.torch_to_f64(x[sl]) for x in (q, k, v, do)), w.scale)[:3]
+        ref = oracle.attention_backward_fp64(*(si.torch_to_f64(x[sl]) for x in (q, k, v, do)), w.scale,
+                                             causal=w.causal)[:3]
         for g, r in zip(grads, ref):
             got = si.torch_to_f64(g[sl])
             errs.append((float(np.max(np.abs(got - r))), float(np.linalg.norm(got - r)), float(np.linalg.norm(r))))
@@ -113,7 +116,7 @@ def cpu_baseline_bwd(w, q, k, v, do, grads, max_heads):
         if time.perf_counter() - t0 > 20.0:
             break
     dt = time.perf_counter() - t0
-    flops = 10.0 * done * w.Nq * w.Nk * w.d
+    flops = 10.0 * done * w.visible_pairs * w.d
     rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / (sum(e[2] ** 2 for e in errs) ** 0.5)
     return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
              "sample": f"{done} of {w.B * w.H} heads (dQ, dK, dV of all {w.Nq} rows) of the same inputs, "
@@ -136,8 +139,9 @@ def main():
     torch.cuda.set_device(0)
     wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16,
           "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16, "bwd": si.BWD_BF16,
+          "bwd_causal": si.BWD_CAUSAL_BF16,
           "headline_f16": si.HEADLINE_F16, "decode_lse": si.DECODE_BF16}[args.workload]
-    is_bwd = args.workload == "bwd"
+    is_bwd = args.workload in ("bwd", "bwd_causal")
     is_decode = args.workload in ("decode", "gqa_decode", "decode_lse")
     lse_form = args.workload == "decode_lse"
 
@@ -182,7 +186,7 @@ def main():
             else:
                 fa.merge_states(pm, pl, po, order=order, out=o)
     elif is_bwd:
-        o, lse = fa.fwd_lse(q, k, v, scale=wl.scale)
+        o, lse = fa.fwd_lse(q, k, v, scale=wl.scale, causal=wl.causal)
         grads = (torch.empty((wl.B, wl.H, wl.Nq, wl.d), device=dev, dtype=torch.float32),
                  torch.empty(k.shape, device=dev, dtype=torch.float32),
                  torch.empty(k.shape, device=dev, dtype=torch.float32),
@@ -191,7 +195,7 @@ def main():
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            fa.bwd(q, k, v, o, dout, lse, scale=wl.scale, out=grads)
+            fa.bwd(q, k, v, o, dout, lse, scale=wl.scale, causal=wl.causal, out=grads)
             if ev is not None:
                 ev[1].record(stream)
     else:
@@ -251,17 +255,21 @@ def main():
             result["dtype"] = wl.dtype
         result["step_bytes"] = step_bytes
     elif is_bwd:
-        flops = 10.0 * wl.B * wl.H * wl.Nq * wl.Nk * wl.d
-        result.update({"metric": ("FA bwd TFLOP/s (10*B*H*N^2*d: the products S, dP, dV, dK, dQ) at N=4096,d=64 "
-                                  "bf16; % of MFMA peak"), "unit": "TFLOP/s",
+        flops = 2.5 * wl.flops   # 10*d per visible pair: the products S, dP, dV, dK, dQ
+        metric = ("FA bwd TFLOP/s (10*B*H*N^2*d: the products S, dP, dV, dK, dQ) at N=4096,d=64 bf16; "
+                  "% of MFMA peak")
+        if wl.causal:
+            metric = ("FA bwd causal TFLOP/s (10*d per visible query-key pair, B*H*N(N+1)/2 pairs) at "
+                      "N=4096,d=64 bf16; % of MFMA peak")
+        result.update({"metric": metric, "unit": "TFLOP/s",
                        "value": flops / (ms_per_step * 1e-3) / 1e12,
                        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
-                                  "causal": False, "grad_dtype": "fp32"}})
+                                  "causal": wl.causal, "grad_dtype": "fp32"}})
         achieved = flops / (avg_launch_ms * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "kernel": "fa_bwd (bwd_delta + bwd_dq + bwd_dkdv)",
                               "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
-                              "traffic": traffic_for("bwd", source_hash("bwd.hip"))}
+                              "traffic": traffic_for(args.workload, source_hash("bwd.hip"))}
     else:
         flops = wl.flops
         tflops = flops / (ms_per_step * 1e-3) / 1e12

@@ -160,9 +160,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
   __shared__ __attribute__((aligned(16))) T lds_v0[C::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_v1[C::ELEMS];
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = CAUSAL ? n_qtiles - 1 - wg % n_qtiles : wg % n_qtiles;
-  const int rest = wg / n_qtiles;
+  // Under the causal mask later query tiles see more keys: the query tile varies slowest in block
+  // order, heaviest first (compute units that finish early take the light tiles). Otherwise the
+  // XCD remap keeps a head's tiles on one L2.
+  int qt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_qtiles;
+    qt = n_qtiles - 1 - (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    qt = wg % n_qtiles;
+    rest = wg / n_qtiles;
+  }
   const int h = rest % a.H;
   const int b = rest / a.H;
   const size_t head = (size_t)b * a.H + h;
@@ -282,9 +292,18 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float lds_d0[kTile];
   __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = wg % n_ktiles;
-  const int rest = wg / n_ktiles;
+  // Under the causal mask earlier key tiles are seen by more query rows: the key tile varies
+  // slowest in block order, heaviest (first) first.
+  int kt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_ktiles;
+    kt = (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    kt = wg % n_ktiles;
+    rest = wg / n_ktiles;
+  }
   const int hk = rest % a.H_kv;
   const int b = rest / a.H_kv;
   const int group = a.H / a.H_kv;

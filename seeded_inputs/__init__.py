@@ -184,6 +184,9 @@ CAUSAL_BF16 = Workload("causal B=4 H=16 N=4096 d=64 bf16", 4, 16, 4096, 4096, 64
 HEADLINE_F16 = Workload("headline_f16 B=4 H=16 N=4096 d=64 fp16", 4, 16, 4096, 4096, 64, "f16", 3)
 # The backward pass on the headline inputs; dL/dO is tensor 3 of the same per-head draws.
 BWD_BF16 = Workload("backward B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 64, "bf16", 3)
+# The backward pass on the causal workload (same draws, the causal mask).
+BWD_CAUSAL_BF16 = Workload("backward causal B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 64, "bf16",
+                           3, causal=True)
 GQA_DECODE_BF16 = Workload("gqa_decode B=16 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 6,
                            num_splits=16, H_kv=8)
 DECODE_BF16 = Workload("split_kv_decode B=16 H=32 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 5,
