@@ -31,6 +31,8 @@
 #include "fa_internal.h"
 #include "mfma_common.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -204,6 +206,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
   const float Dr = a.delta[head * a.Nq + rowc];
   const float c2 = a.scale_log2e;
   const int last_key = CAUSAL ? row + a.causal_off : a.Nk - 1;   // keys past it are masked
+  // the smallest last_key of the wave's rows (its first row's)
+  const int wave_last_key = CAUSAL ? min(qt * kOwn + wave * 32 + a.causal_off, a.Nk - 1) : a.Nk - 1;
 
   f32x16_t acc[C::DB];
 #pragma unroll
@@ -236,23 +240,30 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
         dp[kb] = Mma<T>::mma(row_frag<D, T>(lv, kb * 32 + l32, ks * 2 + hf), dof[ks], dp[kb]);
       }
     // per 16-key step g: P^T = exp(S - L) (0 where masked), dS^T = P^T (dP^T - D), then
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T. At d = 64 only a tile holding a key past the first row's last visible key
+    // (the ragged end; the causal diagonal) takes the per-key mask (a wave-uniform test); at
+    // d = 128 a second copy of the body does not fit in registers.
+    auto grads = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kb = g >> 1;
-      float ds[8];
+      for (int g = 0; g < 4; ++g) {
+        const int kb = g >> 1;
+        float ds[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * (g & 1) + i;
-        const int key = t * kTile + kb * 32 + acc_row(r, hf);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
-        if (key > last_key) p = 0.f;
-        ds[i] = p * (dp[kb][r] - Dr);
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (g & 1) + i;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
+          if constexpr (decltype(masked)::value) {
+            if (t * kTile + kb * 32 + acc_row(r, hf) > last_key) p = 0.f;
+          }
+          ds[i] = p * (dp[kb][r] - Dr);
+        }
+        const v8 dsf = pack8<T>(ds);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag<D, T>(lk, g, db, lane), dsf, acc[db]);
       }
-      const v8 dsf = pack8<T>(ds);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag<D, T>(lk, g, db, lane), dsf, acc[db]);
-    }
+    };
+    if (D > 64 || (t + 1) * kTile - 1 > wave_last_key) grads(std::true_type());  // one body at d = 128
+    else grads(std::false_type());
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -339,6 +350,15 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   const int per_head = n_rtiles - r_begin;
   const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
 
+  // The lse rows are scaled by log2(e) in LDS once per tile (by the wave that loads them, after
+  // its load lands and before the barrier that publishes the tile), so P = 2^(s c - L log2 e)
+  // takes one FMA per element; rows past Nq get L = +inf, so their P is 0 without a mask.
+  auto scale_lse = [&](float* ll, int r0) __attribute__((always_inline)) {
+    if (wave == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      ll[lane] = r0 + lane < a.Nq ? ll[lane] * kLog2e : INFINITY;
+    }
+  };
   auto issue = [&](int step, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
     const int h = hk * group + step / per_head;
     const int r0 = (r_begin + step % per_head) * kTile;
@@ -349,7 +369,10 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     if (wave == 1) load_rowvec(a.delta + head * a.Nq, ld, r0, a.Nq, lane);
   };
 
-  if (n_steps > 0) issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
+  if (n_steps > 0) {
+    issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
+    scale_lse(lds_l0, r_begin * kTile);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -371,38 +394,44 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         s[qb] = Mma<T>::mma(row_frag<D, T>(lq, qb * 32 + l32, ks * 2 + hf), kf[ks], s[qb]);
         dp[qb] = Mma<T>::mma(row_frag<D, T>(ldo, qb * 32 + l32, ks * 2 + hf), vf[ks], dp[qb]);
       }
-    // per 16-row step g: P = exp(S - L) (0 for rows past Nq and masked keys), dS = P (dP - D),
-    // then dV^T += dO^T P and dK^T += Q^T dS
+    // per 16-row step g: P = exp(S - L) (0 for rows past Nq, whose L is +inf, and for masked
+    // keys), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS. Under the causal mask,
+    // register r of lane half hf holds row r0 + 32 qb + acc_row(r, hf), which sees this lane's key
+    // when 32 qb + 8 (r / 4) + r % 4 >= key - causal_off - r0 - 4 hf (= lim).
+    int lim = 0;
+    if constexpr (CAUSAL) lim = key - a.causal_off - r0 - 4 * hf;
+    {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qb = g >> 1;
-      float p[8], ds[8];
+      for (int g = 0; g < 4; ++g) {
+        const int qb = g >> 1;
+        float p[8], ds[8];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int g4 = 2 * (g & 1) + h2;
-        const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
-        const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&ll[i0]);
-        const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&ld[i0]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int g4 = 2 * (g & 1) + h2;
+          const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
+          const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&ll[i0]);   // lse * log2(e)
+          const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&ld[i0]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * g4 + u;
-          const int qrow = r0 + i0 + u;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u] * kLog2e));
-          bool live = qrow < a.Nq;
-          if constexpr (CAUSAL) live = live && key <= qrow + a.causal_off;
-          if (!live) x = 0.f;
-          p[4 * h2 + u] = x;
-          ds[4 * h2 + u] = x * (dp[qb][r] - Dv[u]);
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * g4 + u;
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u]));
+            if constexpr (CAUSAL) {
+              if (32 * qb + 8 * g4 + u < lim) x = 0.f;
+            }
+            p[4 * h2 + u] = x;
+            ds[4 * h2 + u] = x * (dp[qb][r] - Dv[u]);
+          }
+        }
+        const v8 pf = pack8<T>(p);
+        const v8 dsf = pack8<T>(ds);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          dv[db] = Mma<T>::mma(tr_frag<D, T>(ldo, g, db, lane), pf, dv[db]);
+          dk[db] = Mma<T>::mma(tr_frag<D, T>(lq, g, db, lane), dsf, dk[db]);
         }
       }
-      const v8 pf = pack8<T>(p);
-      const v8 dsf = pack8<T>(ds);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        dv[db] = Mma<T>::mma(tr_frag<D, T>(ldo, g, db, lane), pf, dv[db]);
-        dk[db] = Mma<T>::mma(tr_frag<D, T>(lq, g, db, lane), dsf, dk[db]);
-      }
     }
+    if (st + 1 < n_steps) scale_lse(nl, (r_begin + (st + 1) % per_head) * kTile);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
