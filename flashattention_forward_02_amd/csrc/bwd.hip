@@ -350,13 +350,18 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   const int per_head = n_rtiles - r_begin;
   const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
 
-  // The lse rows are scaled by log2(e) in LDS once per tile (by the wave that loads them, after
-  // its load lands and before the barrier that publishes the tile), so P = 2^(s c - L log2 e)
-  // takes one FMA per element; rows past Nq get L = +inf, so their P is 0 without a mask.
-  auto scale_lse = [&](float* ll, int r0) __attribute__((always_inline)) {
+  // The row values are prepared in LDS once per tile by the waves that load them (after the load
+  // lands, before the barrier that publishes the tile): lse scaled by log2(e), so P = 2^(s c -
+  // L log2 e) takes one FMA per element, and +inf for rows past Nq, so their P is 0 without a
+  // mask; D negated, as the initial value of the dP accumulator (dP - D comes out of the MFMAs).
+  auto prep_rows = [&](float* ll, float* ld, int r0) __attribute__((always_inline)) {
     if (wave == 0) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       ll[lane] = r0 + lane < a.Nq ? ll[lane] * kLog2e : INFINITY;
+    }
+    if (wave == 1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      ld[lane] = -ld[lane];
     }
   };
   auto issue = [&](int step, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
   if (n_steps > 0) {
     issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
-    scale_lse(lds_l0, r_begin * kTile);
+    prep_rows(lds_l0, lds_d0, r_begin * kTile);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -381,12 +386,21 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                   float* nd) __attribute__((always_inline)) {
     if (st + 1 < n_steps) issue(st + 1, nq, ndo, nl, nd);
     const int r0 = (r_begin + st % per_head) * kTile;
-    // S = Q K^T and dP = dO V^T: rows = the tile's 64 query rows (two 32-blocks), columns = keys
+    // S = Q K^T and dP - D = dO V^T - D: rows = the tile's 64 query rows (two 32-blocks),
+    // columns = keys. Register r of lane half hf is row 32 qb + acc_row(r, hf): registers
+    // 4 g4 .. 4 g4 + 3 are four consecutive rows, one 16-byte read of -D.
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4_t nD = *reinterpret_cast<const f32x4_t*>(&ld[qb * 32 + 8 * g4 + 4 * hf]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s[qb][4 * g4 + u] = 0.f;
+          dp[qb][4 * g4 + u] = nD[u];
+        }
+      }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
@@ -410,7 +424,6 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
           const int g4 = 2 * (g & 1) + h2;
           const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
           const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&ll[i0]);   // lse * log2(e)
-          const f32x4_t Dv = *reinterpret_cast<const f32x4_t*>(&ld[i0]);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * g4 + u;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
               if (32 * qb + 8 * g4 + u < lim) x = 0.f;
             }
             p[4 * h2 + u] = x;
-            ds[4 * h2 + u] = x * (dp[qb][r] - Dv[u]);
+            ds[4 * h2 + u] = x * dp[qb][r];
           }
         }
         const v8 pf = pack8<T>(p);
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         }
       }
     }
-    if (st + 1 < n_steps) scale_lse(nl, (r_begin + (st + 1) % per_head) * kTile);
+    if (st + 1 < n_steps) prep_rows(nl, nd, (r_begin + (st + 1) % per_head) * kTile);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
