@@ -232,6 +232,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+    // The two waves of a SIMD come from different workgroups and drift in and out of step; the
+    // raised priority lets a wave's S / dP burst issue ahead of the other wave's VALU work
+    // (measured 1.5 % faster).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
@@ -239,6 +243,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
         s[kb] = Mma<T>::mma(row_frag<D, T>(lk, kb * 32 + l32, ks * 2 + hf), qf[ks], s[kb]);
         dp[kb] = Mma<T>::mma(row_frag<D, T>(lv, kb * 32 + l32, ks * 2 + hf), dof[ks], dp[kb]);
       }
+    __builtin_amdgcn_s_setprio(0);
     // per 16-key step g: P^T = exp(S - L) (0 where masked), dS^T = P^T (dP^T - D), then
     // dQ^T += K^T dS^T. At d = 64 only a tile holding a key past the first row's last visible key
     // (the ragged end; the causal diagonal) takes the per-key mask (a wave-uniform test); at
@@ -401,6 +406,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
           dp[qb][4 * g4 + u] = nD[u];
         }
       }
+    __builtin_amdgcn_s_setprio(1);   // as in bwd_dq_kernel
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
@@ -408,6 +414,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         s[qb] = Mma<T>::mma(row_frag<D, T>(lq, qb * 32 + l32, ks * 2 + hf), kf[ks], s[qb]);
         dp[qb] = Mma<T>::mma(row_frag<D, T>(ldo, qb * 32 + l32, ks * 2 + hf), vf[ks], dp[qb]);
       }
+    __builtin_amdgcn_s_setprio(0);
     // per 16-row step g: P = exp(S - L) (0 for rows past Nq, whose L is +inf, and for masked
     // keys), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS. Under the causal mask,
     // register r of lane half hf holds row r0 + 32 qb + acc_row(r, hf), which sees this lane's key
