@@ -118,6 +118,52 @@ __device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[8]) {
 // Row index (within a 32-row block) of register r of lane half hf in a 32x32 accumulator.
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
+// This lane's byte offsets of the row_frag and tr_frag reads within a tile. The swizzle of a row
+// depends only on (row / 2) % 8, so a row read at row + 32 qb and a transposing read at rows
+// + 16 g are these offsets plus a constant (64 qb D or 32 g D bytes), which the reads take as an
+// immediate. Kernels pass the offsets through an empty asm once per step, so the compiler cannot
+// hoist one register per (buffer, read) out of the loop.
+template <int D, typename T>
+struct LdsOff {
+  unsigned row[D / 16];                  // row_frag(lx, l32, 2 ks + hf)
+  unsigned tr1[D / 32], tr2[D / 32];     // tr_frag(lx, 0, db): the two 8-byte transposing reads
+  __device__ __forceinline__ LdsOff(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = (unsigned)((l32 * D + (((ks * 2 + hf) ^ swzk(l32)) << 3)) * sizeof(T));
+    const int tj = lane & 15, ti = tj >> 2, tq = tj & 3, tgb = (lane >> 4) & 1;
+    const int row1 = 4 * hf + ti;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + tgb * 16 + tq * 4;
+      tr1[db] = (unsigned)((row1 * D + (((col >> 3) ^ swzk(row1)) << 3) + (col & 7)) * sizeof(T));
+      tr2[db] = (unsigned)(((row1 + 8) * D + (((col >> 3) ^ swzk(row1 + 8)) << 3) + (col & 7)) * sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(row[i]));
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(tr1[i]), "+v"(tr2[i]));
+  }
+};
+// row_frag(lx, 32 qb + l32, 2 ks + hf) from the offsets
+template <int D, typename T>
+__device__ __forceinline__ typename Mma<T>::v8 row_frag_o(const T* lx, const LdsOff<D, T>& o, int qb, int ks) {
+  const char* p = reinterpret_cast<const char*>(lx) + o.row[ks] + qb * 32 * D * (int)sizeof(T);
+  return *reinterpret_cast<const typename Mma<T>::v8*>(p);
+}
+// tr_frag(lx, g, db, lane) from the offsets
+template <int D, typename T>
+__device__ __forceinline__ typename Mma<T>::v8 tr_frag_o(const T* lx, const LdsOff<D, T>& o, int g, int db) {
+  const char* base = reinterpret_cast<const char*>(lx) + g * 16 * D * (int)sizeof(T);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + o.tr1[db]));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + o.tr2[db]));
+  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+  const u32x4_t packed = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(typename Mma<T>::v8, packed);
+}
+
 // ---------------------------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic
 // ---------------------------------------------------------------------------------------------
@@ -220,8 +266,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  LdsOff<D, T> lo0(lane);
   // One key tile: prefetch tile t + 1 into (nk, nv), compute from (lk, lv), wait, barrier.
   auto tile = [&](int t, const T* lk, const T* lv, T* nk, T* nv) __attribute__((always_inline)) {
+    LdsOff<D, T> lo = lo0;
+    lo.opaque();
     if (t + 1 < T_) {
       load_tile<D, T>(K, nk, (t + 1) * kTile, a.Nk, wave, lane);
       load_tile<D, T>(V, nv, (t + 1) * kTile, a.Nk, wave, lane);
@@ -240,8 +289,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = Mma<T>::mma(row_frag<D, T>(lk, kb * 32 + l32, ks * 2 + hf), qf[ks], s[kb]);
-        dp[kb] = Mma<T>::mma(row_frag<D, T>(lv, kb * 32 + l32, ks * 2 + hf), dof[ks], dp[kb]);
+        s[kb] = Mma<T>::mma(row_frag_o<D, T>(lk, lo, kb, ks), qf[ks], s[kb]);
+        dp[kb] = Mma<T>::mma(row_frag_o<D, T>(lv, lo, kb, ks), dof[ks], dp[kb]);
       }
     __builtin_amdgcn_s_setprio(0);
     // per 16-key step g: P^T = exp(S - L) (0 where masked), dS^T = P^T (dP^T - D), then
@@ -264,7 +313,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
         }
         const v8 dsf = pack8<T>(ds);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag<D, T>(lk, g, db, lane), dsf, acc[db]);
+        for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag_o<D, T>(lk, lo, g, db), dsf, acc[db]);
       }
     };
     if (D > 64 || (t + 1) * kTile - 1 > wave_last_key) grads(std::true_type());  // one body at d = 128
@@ -387,8 +436,11 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   __syncthreads();
 
   // One (query head, row tile) step: prefetch the next into the other buffers, compute, wait, barrier.
+  LdsOff<D, T> lo0(lane);
   auto step = [&](int st, const T* lq, const T* ldo, const float* ll, const float* ld, T* nq, T* ndo, float* nl,
                   float* nd) __attribute__((always_inline)) {
+    LdsOff<D, T> lo = lo0;
+    lo.opaque();
     if (st + 1 < n_steps) issue(st + 1, nq, ndo, nl, nd);
     const int r0 = (r_begin + st % per_head) * kTile;
     // S = Q K^T and dP - D = dO V^T - D: rows = the tile's 64 query rows (two 32-blocks),
@@ -411,8 +463,8 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = Mma<T>::mma(row_frag<D, T>(lq, qb * 32 + l32, ks * 2 + hf), kf[ks], s[qb]);
-        dp[qb] = Mma<T>::mma(row_frag<D, T>(ldo, qb * 32 + l32, ks * 2 + hf), vf[ks], dp[qb]);
+        s[qb] = Mma<T>::mma(row_frag_o<D, T>(lq, lo, qb, ks), kf[ks], s[qb]);
+        dp[qb] = Mma<T>::mma(row_frag_o<D, T>(ldo, lo, qb, ks), vf[ks], dp[qb]);
       }
     __builtin_amdgcn_s_setprio(0);
     // per 16-row step g: P = exp(S - L) (0 for rows past Nq, whose L is +inf, and for masked
@@ -446,8 +498,8 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const v8 dsf = pack8<T>(ds);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          dv[db] = Mma<T>::mma(tr_frag<D, T>(ldo, g, db, lane), pf, dv[db]);
-          dk[db] = Mma<T>::mma(tr_frag<D, T>(lq, g, db, lane), dsf, dk[db]);
+          dv[db] = Mma<T>::mma(tr_frag_o<D, T>(ldo, lo, g, db), pf, dv[db]);
+          dk[db] = Mma<T>::mma(tr_frag_o<D, T>(lq, lo, g, db), dsf, dk[db]);
         }
       }
     }
