@@ -529,6 +529,281 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dK, dV at d = 64, ping-pong: 8 waves in two groups (A = waves 0-3, B = 4-7; waves w and w + 4
+// share a SIMD) in opposite phases, as in the forward kernel, so one wave of each SIMD keeps the
+// matrix core busy while the other computes P and dS. A workgroup owns 256 keys of one
+// (b, h_kv), 32 per wave, and streams the 64-row query tiles of every query head of the group.
+//   MFMA phase of step t: dV^T += dO^T P and dK^T += Q^T dS of step t - 1, then S and dP - D of
+//     step t.
+//   VALU phase of step t: P and dS of step t, rounded as the next phase's B operands.
+// Group B runs one phase behind group A. Group A loads the tiles of step t + 1 (Q, dO, L, D) at
+// the top of its MFMA phase t and waits for them at the end of its VALU phase t; a tile is read
+// in MFMA phases t (rows) and t + 1 (transposed), so three buffers rotate: the load into buffer
+// (t + 1) % 3 starts after both groups' last reads of step t - 2, which ended at least one barrier
+// earlier. The steady steps are unrolled by three so every buffer is a distinct object at each use.
+// ---------------------------------------------------------------------------------------------
+constexpr int kPpWaves = 8;
+constexpr int kPpOwn = kPpWaves * 32;            // keys per workgroup
+
+// Issue order of a full MFMA phase (16 dV / dK MFMAs fed by two transposing reads each, then the
+// 8 reads of -D, then 16 S / dP MFMAs fed by one row read each): the reads of the MFMA PD
+// positions ahead go before each MFMA, so LDS latency hides behind matrix-core work and only a
+// few operands are in registers at once.
+__host__ __device__ constexpr int pp_reads_needed(int i) { return i < 16 ? 2 * (i + 1) : 40 + (i - 15); }
+template <int PD, int I>
+__device__ __forceinline__ void dkdv_pp_order() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NM = 32;
+  constexpr int kMfma = 0x008, kDsRead = 0x100;  // sched_group_barrier instruction classes
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, pp_reads_needed(PD), 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    constexpr int a = pp_reads_needed(I + PD < NM ? I + PD : NM - 1);
+    constexpr int b = pp_reads_needed(I + 1 + PD < NM ? I + 1 + PD : NM - 1);
+    if constexpr (b > a) __builtin_amdgcn_sched_group_barrier(kDsRead, b - a, 0);
+    dkdv_pp_order<PD, I + 1>();
+  }
+#endif
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int D = 64;
+  typedef BCfg<D, T> C;
+  typedef typename C::v8 v8;
+  __shared__ __attribute__((aligned(16))) T lds_q0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_q1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_q2[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do2[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) float lds_l0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_l1[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_l2[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d2[kTile];
+
+  // work order as in bwd_dkdv_kernel
+  int kt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_ktiles;
+    kt = (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    kt = wg % n_ktiles;
+    rest = wg / n_ktiles;
+  }
+  const int hk = rest % a.H_kv;
+  const int b = rest / a.H_kv;
+  const int group = a.H / a.H_kv;
+  const size_t kvh = (size_t)b * a.H_kv + hk;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool group_a = wave < 4;
+  const int gw = wave & 3;                         // wave index within its group (loads: group A)
+  const int hf = lane >> 5;
+  const int key = kt * kPpOwn + wave * 32 + (lane & 31);   // this lane's key (column of S)
+  const int keyc = min(key, a.Nk - 1);
+
+  v8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)keyc * D + ks * 16 + hf * 8);
+    vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)keyc * D + ks * 16 + hf * 8);
+  }
+  const float c2 = a.scale_log2e;
+
+  f32x16_t dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
+
+  const int n_rtiles = (a.Nq + kTile - 1) / kTile;
+  int r_begin = 0;
+  if constexpr (CAUSAL) r_begin = max(0, kt * kPpOwn - a.causal_off) / kTile;
+  const int per_head = n_rtiles - r_begin;
+  const int n_steps = per_head * group;            // (query head, row tile) pairs, head-major
+  auto row0 = [&](int st) { return (r_begin + st % per_head) * kTile; };
+
+  // Group A: a quarter of each tile per wave (a whole tile: scalar base and per-lane 32-bit
+  // offsets computed once, kept opaque; a tile past Nq: load_tile's clamped path); wave 0 the lse
+  // rows, wave 1 the D rows.
+  unsigned toff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int ci = (gw * C::LPW + i) * 64 + lane;
+    const int r = ci / C::CH, cpos = ci % C::CH;
+    toff[i] = (unsigned)((r * D + ((cpos ^ swzk(r)) << 3)) * sizeof(T));
+  }
+  auto tile_in = [&](const T* X, T* lx, int r0) __attribute__((always_inline)) {
+    if (r0 + kTile <= a.Nq) {
+      const char* g = reinterpret_cast<const char*>(X + (size_t)r0 * D);
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        unsigned o = toff[i];
+        asm volatile("" : "+v"(o));
+        global_to_lds16(g + o, &lx[(gw * C::LPW + i) * 64 * 8]);
+      }
+    } else {
+      load_tile<D, T>(X, lx, r0, a.Nq, gw, lane);
+    }
+  };
+  auto issue = [&](int st, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
+    const int h = hk * group + st / per_head;
+    const int r0 = row0(st);
+    const size_t head = (size_t)b * a.H + h;
+    tile_in(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lq, r0);
+    tile_in(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, ldo, r0);
+    if (wave == 0) load_rowvec(a.lse + head * a.Nq, ll, r0, a.Nq, lane);
+    if (wave == 1) load_rowvec(a.delta + head * a.Nq, ld, r0, a.Nq, lane);
+  };
+  // After the loads land (vmcnt(0) of the loading wave): lse * log2(e) (+inf past Nq), and -D.
+  auto prep_rows = [&](float* ll, float* ld, int r0) __attribute__((always_inline)) {
+    if (wave == 0) ll[lane] = r0 + lane < a.Nq ? ll[lane] * kLog2e : INFINITY;
+    if (wave == 1) ld[lane] = -ld[lane];
+  };
+
+  const LdsOff<D, T> lo0(lane);
+  f32x16_t s[2], dp[2];
+  v8 pf[4], dsf[4];
+
+  // do_dkdv / do_sdp are compile-time flags (std::true_type / std::false_type), so the issue
+  // order sits in the same basic block as the reads and MFMAs it orders.
+  auto phase_mfma = [&](int t, auto do_dkdv, auto do_sdp, const T* qp, const T* dop, const T* qc, const T* doc,
+                        const float* dc, T* qn, T* don, float* ln, float* dn) __attribute__((always_inline)) {
+    LdsOff<D, T> lo = lo0;
+    lo.opaque();
+    if (group_a && t + 1 < n_steps) issue(t + 1, qn, don, ln, dn);
+    if constexpr (decltype(do_dkdv)::value) {
+      // dV^T += dO^T P and dK^T += Q^T dS of step t - 1 (transposing reads of its tiles)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          dv[db] = Mma<T>::mma(tr_frag_o<D, T>(dop, lo, g, db), pf[g], dv[db]);
+          dk[db] = Mma<T>::mma(tr_frag_o<D, T>(qp, lo, g, db), dsf[g], dk[db]);
+        }
+    }
+    if constexpr (decltype(do_sdp)::value) {
+      // S = Q K^T and dP - D = dO V^T - D of step t (the dP accumulator starts at -D)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4_t nD = *reinterpret_cast<const f32x4_t*>(&dc[qb * 32 + 8 * g4 + 4 * hf]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            s[qb][4 * g4 + u] = 0.f;
+            dp[qb][4 * g4 + u] = nD[u];
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = Mma<T>::mma(row_frag_o<D, T>(qc, lo, qb, ks), kf[ks], s[qb]);
+          dp[qb] = Mma<T>::mma(row_frag_o<D, T>(doc, lo, qb, ks), vf[ks], dp[qb]);
+        }
+    }
+    if constexpr (decltype(do_dkdv)::value && decltype(do_sdp)::value) dkdv_pp_order<6, 0>();
+    __syncthreads();
+  };
+
+  auto phase_valu = [&](int t, const float* lc, float* ln, float* dn) __attribute__((always_inline)) {
+    // P = exp(S - L) (0 past Nq through L = +inf; masked keys), dS = P (dP - D), as in
+    // bwd_dkdv_kernel (register r of lane half hf is row 32 qb + acc_row(r, hf))
+    const int r0 = row0(t);
+    int lim = 0;
+    if constexpr (CAUSAL) lim = key - a.causal_off - r0 - 4 * hf;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qb = g >> 1;
+      float p[8], ds[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int g4 = 2 * (g & 1) + h2;
+        const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&lc[qb * 32 + 8 * g4 + 4 * hf]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g4 + u;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u]));
+          if constexpr (CAUSAL) {
+            if (32 * qb + 8 * g4 + u < lim) x = 0.f;
+          }
+          p[4 * h2 + u] = x;
+          ds[4 * h2 + u] = x * dp[qb][r];
+        }
+      }
+      pf[g] = pack8<T>(p);
+      dsf[g] = pack8<T>(ds);
+    }
+    if (group_a) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (t + 1 < n_steps) prep_rows(ln, dn, row0(t + 1));
+    }
+    __syncthreads();
+  };
+
+  // prologue: step 0's tiles resident and prepared; group B then sits out one phase
+  if (group_a && n_steps > 0) {
+    issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    prep_rows(lds_l0, lds_d0, row0(0));
+  }
+  __syncthreads();
+  if (!group_a) __syncthreads();
+
+  // Step t reads buffers t % 3 (its own tiles) and (t + 2) % 3 (step t - 1's, transposed) and
+  // loads into (t + 1) % 3: step 0 (S / dP only), the steady steps unrolled by three, then the
+  // last step's dV / dK. Every wave takes the same number of barriers.
+  const std::true_type yes;
+  const std::false_type no;
+  if (n_steps > 0) {
+    phase_mfma(0, no, yes, lds_q2, lds_do2, lds_q0, lds_do0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+    phase_valu(0, lds_l0, lds_l1, lds_d1);
+  }
+  for (int t = 1; t < n_steps; t += 3) {
+    phase_mfma(t, yes, yes, lds_q0, lds_do0, lds_q1, lds_do1, lds_d1, lds_q2, lds_do2, lds_l2, lds_d2);
+    phase_valu(t, lds_l1, lds_l2, lds_d2);
+    if (t + 1 < n_steps) {
+      phase_mfma(t + 1, yes, yes, lds_q1, lds_do1, lds_q2, lds_do2, lds_d2, lds_q0, lds_do0, lds_l0, lds_d0);
+      phase_valu(t + 1, lds_l2, lds_l0, lds_d0);
+    }
+    if (t + 2 < n_steps) {
+      phase_mfma(t + 2, yes, yes, lds_q2, lds_do2, lds_q0, lds_do0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+      phase_valu(t + 2, lds_l0, lds_l1, lds_d1);
+    }
+  }
+  if (n_steps == 0) phase_mfma(0, no, no, lds_q0, lds_do0, lds_q0, lds_do0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+  else if ((n_steps - 1) % 3 == 0) phase_mfma(n_steps, yes, no, lds_q0, lds_do0, lds_q1, lds_do1, lds_d1, lds_q2, lds_do2, lds_l2, lds_d2);
+  else if ((n_steps - 1) % 3 == 1) phase_mfma(n_steps, yes, no, lds_q1, lds_do1, lds_q2, lds_do2, lds_d2, lds_q0, lds_do0, lds_l0, lds_d0);
+  else phase_mfma(n_steps, yes, no, lds_q2, lds_do2, lds_q0, lds_do0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+  if (group_a) __syncthreads();
+
+  if (key < a.Nk) {
+    float* outk = a.dk + (kvh * (size_t)a.Nk + key) * D;
+    float* outv = a.dv + (kvh * (size_t)a.Nk + key) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = db * 32 + 8 * g4 + 4 * hf;
+        f32x4_t xk = {a.scale * dk[db][4 * g4], a.scale * dk[db][4 * g4 + 1], a.scale * dk[db][4 * g4 + 2],
+                      a.scale * dk[db][4 * g4 + 3]};
+        f32x4_t xv = {dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(outk + dd) = xk;
+        *reinterpret_cast<f32x4_t*>(outv + dd) = xv;
+      }
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.Nq;
@@ -553,11 +828,20 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (nk == 0) return hipSuccess;
-  int n = n_ktiles;
-  void* kargs[] = {&args, &n};
-  const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, true>)
-                           : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, false>);
-  return hipLaunchKernel(k, dim3((unsigned)nk), dim3(kBwdThreads), kargs, 0, s);
+  if constexpr (D == 64) {  // ping-pong kernel: 256 keys per workgroup
+    int n = (a.Nk + kPpOwn - 1) / kPpOwn;
+    const long long nkp = (long long)n * a.H_kv * a.B;
+    void* kargs[] = {&args, &n};
+    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_pp_kernel<T, true>)
+                             : reinterpret_cast<const void*>(&bwd_dkdv_pp_kernel<T, false>);
+    return hipLaunchKernel(k, dim3((unsigned)nkp), dim3(kPpWaves * 64), kargs, 0, s);
+  } else {
+    int n = n_ktiles;
+    void* kargs[] = {&args, &n};
+    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, true>)
+                             : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, false>);
+    return hipLaunchKernel(k, dim3((unsigned)nk), dim3(kBwdThreads), kargs, 0, s);
+  }
 }
 
 }  // namespace
