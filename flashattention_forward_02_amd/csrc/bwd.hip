@@ -804,6 +804,232 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dQ at d = 64, ping-pong (the structure of bwd_dkdv_pp_kernel with the roles of queries and keys
+// exchanged): a workgroup owns 256 query rows of one (b, h), 32 per wave, and streams the head's
+// K and V in 64-key tiles.
+//   MFMA phase of tile t: dQ^T += K^T dS^T of tile t - 1, then S^T = K Q^T and dP^T - D of tile t.
+//   VALU phase of tile t: P^T and dS^T of tile t.
+// K is read in MFMA phases t (rows) and t + 1 (transposed), so the tiles rotate through three
+// buffers as in bwd_dkdv_pp_kernel.
+// ---------------------------------------------------------------------------------------------
+__host__ __device__ constexpr int dq_pp_reads_needed(int i) { return i < 8 ? 2 * (i + 1) : 16 + (i - 7); }
+template <int PD, int I>
+__device__ __forceinline__ void dq_pp_order() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NM = 24;
+  constexpr int kMfma = 0x008, kDsRead = 0x100;  // sched_group_barrier instruction classes
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, dq_pp_reads_needed(PD), 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    constexpr int a = dq_pp_reads_needed(I + PD < NM ? I + PD : NM - 1);
+    constexpr int b = dq_pp_reads_needed(I + 1 + PD < NM ? I + 1 + PD : NM - 1);
+    if constexpr (b > a) __builtin_amdgcn_sched_group_barrier(kDsRead, b - a, 0);
+    dq_pp_order<PD, I + 1>();
+  }
+#endif
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dq_pp_kernel(BwdArgs a, int n_qtiles) {
+  constexpr int D = 64;
+  typedef BCfg<D, T> C;
+  typedef typename C::v8 v8;
+  __shared__ __attribute__((aligned(16))) T lds_k0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_k1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_k2[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v2[C::ELEMS];
+
+  // work order as in bwd_dq_kernel
+  int qt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_qtiles;
+    qt = n_qtiles - 1 - (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    qt = wg % n_qtiles;
+    rest = wg / n_qtiles;
+  }
+  const int h = rest % a.H;
+  const int b = rest / a.H;
+  const size_t head = (size_t)b * a.H + h;
+  const size_t kvh = kv_head_index(b, h, a.H, a.H_kv);
+  const T* __restrict__ Q = static_cast<const T*>(a.q) + head * (size_t)a.Nq * D;
+  const T* __restrict__ dO = static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool group_a = wave < 4;
+  const int gw = wave & 3;
+  const int hf = lane >> 5;
+  const int row = qt * kPpOwn + wave * 32 + (lane & 31);   // this lane's query row (column of S^T)
+  const int rowc = min(row, a.Nq - 1);
+
+  int kend = a.Nk;
+  if constexpr (CAUSAL) kend = min(kend, min(a.Nq, (qt + 1) * kPpOwn) + a.causal_off);
+  const int T_ = (kend + kTile - 1) / kTile;
+
+  v8 qf[C::KS], dof[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)rowc * D + ks * 16 + hf * 8);
+    dof[ks] = *reinterpret_cast<const v8*>(dO + (size_t)rowc * D + ks * 16 + hf * 8);
+  }
+  const float L2 = a.lse[head * a.Nq + rowc] * kLog2e;
+  const float nDr = -a.delta[head * a.Nq + rowc];
+  const float c2 = a.scale_log2e;
+  const int last_key = CAUSAL ? row + a.causal_off : a.Nk - 1;   // keys past it are masked
+  const int wave_last_key = CAUSAL ? min(qt * kPpOwn + wave * 32 + a.causal_off, a.Nk - 1) : a.Nk - 1;
+
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  // Group A loads a quarter of each tile per wave (whole tiles: scalar base + opaque 32-bit
+  // offsets; the ragged end: load_tile's clamped path).
+  unsigned toff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int ci = (gw * C::LPW + i) * 64 + lane;
+    const int r = ci / C::CH, cpos = ci % C::CH;
+    toff[i] = (unsigned)((r * D + ((cpos ^ swzk(r)) << 3)) * sizeof(T));
+  }
+  auto tile_in = [&](const T* X, T* lx, int k0) __attribute__((always_inline)) {
+    if (k0 + kTile <= a.Nk) {
+      const char* g = reinterpret_cast<const char*>(X + (size_t)k0 * D);
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        unsigned o = toff[i];
+        asm volatile("" : "+v"(o));
+        global_to_lds16(g + o, &lx[(gw * C::LPW + i) * 64 * 8]);
+      }
+    } else {
+      load_tile<D, T>(X, lx, k0, a.Nk, gw, lane);
+    }
+  };
+  auto issue = [&](int t, T* lk, T* lv) __attribute__((always_inline)) {
+    tile_in(K, lk, t * kTile);
+    tile_in(V, lv, t * kTile);
+  };
+
+  const LdsOff<D, T> lo0(lane);
+  f32x16_t s[2], dp[2];
+  v8 dsf[4];
+
+  auto phase_mfma = [&](int t, auto do_dq, auto do_sdp, const T* kp, const T* kc, const T* vc, T* kn, T* vn)
+      __attribute__((always_inline)) {
+    LdsOff<D, T> lo = lo0;
+    lo.opaque();
+    if (group_a && t + 1 < T_) issue(t + 1, kn, vn);
+    if constexpr (decltype(do_dq)::value) {
+      // dQ^T += K^T dS^T of tile t - 1 (transposing reads of its K tile)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] = Mma<T>::mma(tr_frag_o<D, T>(kp, lo, g, db), dsf[g], acc[db]);
+    }
+    if constexpr (decltype(do_sdp)::value) {
+      // S^T = K Q^T and dP^T - D = V dO^T - D of tile t (the dP accumulator starts at -D)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 0.f;
+          dp[kb][r] = nDr;
+        }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = Mma<T>::mma(row_frag_o<D, T>(kc, lo, kb, ks), qf[ks], s[kb]);
+          dp[kb] = Mma<T>::mma(row_frag_o<D, T>(vc, lo, kb, ks), dof[ks], dp[kb]);
+        }
+    }
+    if constexpr (decltype(do_dq)::value && decltype(do_sdp)::value) dq_pp_order<6, 0>();
+    __syncthreads();
+  };
+
+  auto phase_valu = [&](int t) __attribute__((always_inline)) {
+    // per 16-key step g: P^T = exp(S - L), dS^T = P^T (dP^T - D); only a tile holding a key past
+    // the wave's first row's last visible key takes the per-key mask (a wave-uniform test)
+    auto grads = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kb = g >> 1;
+        float ds[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (g & 1) + i;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -L2));
+          if constexpr (decltype(masked)::value) {
+            if (t * kTile + kb * 32 + acc_row(r, hf) > last_key) p = 0.f;
+          }
+          ds[i] = p * dp[kb][r];
+        }
+        dsf[g] = pack8<T>(ds);
+      }
+    };
+    if ((t + 1) * kTile - 1 > wave_last_key) grads(std::true_type());
+    else grads(std::false_type());
+    if (group_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // prologue: tile 0 resident; group B then sits out one phase
+  if (group_a && T_ > 0) {
+    issue(0, lds_k0, lds_v0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  if (!group_a) __syncthreads();
+
+  // Tile t reads buffers t % 3 and (t + 2) % 3 (tile t - 1's K, transposed) and loads into
+  // (t + 1) % 3: tile 0 (S / dP only), the steady tiles unrolled by three, then the last dQ.
+  const std::true_type yes;
+  const std::false_type no;
+  if (T_ > 0) {
+    phase_mfma(0, no, yes, lds_k2, lds_k0, lds_v0, lds_k1, lds_v1);
+    phase_valu(0);
+  }
+  for (int t = 1; t < T_; t += 3) {
+    phase_mfma(t, yes, yes, lds_k0, lds_k1, lds_v1, lds_k2, lds_v2);
+    phase_valu(t);
+    if (t + 1 < T_) {
+      phase_mfma(t + 1, yes, yes, lds_k1, lds_k2, lds_v2, lds_k0, lds_v0);
+      phase_valu(t + 1);
+    }
+    if (t + 2 < T_) {
+      phase_mfma(t + 2, yes, yes, lds_k2, lds_k0, lds_v0, lds_k1, lds_v1);
+      phase_valu(t + 2);
+    }
+  }
+  if (T_ == 0) phase_mfma(0, no, no, lds_k0, lds_k0, lds_v0, lds_k1, lds_v1);
+  else if ((T_ - 1) % 3 == 0) phase_mfma(T_, yes, no, lds_k0, lds_k1, lds_v1, lds_k2, lds_v2);
+  else if ((T_ - 1) % 3 == 1) phase_mfma(T_, yes, no, lds_k1, lds_k2, lds_v2, lds_k0, lds_v0);
+  else phase_mfma(T_, yes, no, lds_k2, lds_k0, lds_v0, lds_k1, lds_v1);
+  if (group_a) __syncthreads();
+
+  if (row < a.Nq) {
+    float* out = a.dq + (head * (size_t)a.Nq + row) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = db * 32 + 8 * g4 + 4 * hf;
+        f32x4_t x = {a.scale * acc[db][4 * g4], a.scale * acc[db][4 * g4 + 1], a.scale * acc[db][4 * g4 + 2],
+                     a.scale * acc[db][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(out + dd) = x;
+      }
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.Nq;
@@ -820,11 +1046,20 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, T>), dim3((unsigned)nd),
                                    dim3(256), kargs, 0, s);
     if (e != hipSuccess) return e;
-    int n = n_qtiles;
-    void* kargs2[] = {&args, &n};
-    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, true>)
-                             : reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, false>);
-    e = hipLaunchKernel(k, dim3((unsigned)nq), dim3(kBwdThreads), kargs2, 0, s);
+    if constexpr (D == 64) {  // ping-pong kernel: 256 query rows per workgroup
+      int n = (a.Nq + kPpOwn - 1) / kPpOwn;
+      const long long nqp = (long long)n * a.H * a.B;
+      void* kargs2[] = {&args, &n};
+      const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dq_pp_kernel<T, true>)
+                               : reinterpret_cast<const void*>(&bwd_dq_pp_kernel<T, false>);
+      e = hipLaunchKernel(k, dim3((unsigned)nqp), dim3(kPpWaves * 64), kargs2, 0, s);
+    } else {
+      int n = n_qtiles;
+      void* kargs2[] = {&args, &n};
+      const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, true>)
+                               : reinterpret_cast<const void*>(&bwd_dq_kernel<D, T, false>);
+      e = hipLaunchKernel(k, dim3((unsigned)nq), dim3(kBwdThreads), kargs2, 0, s);
+    }
     if (e != hipSuccess) return e;
   }
   if (nk == 0) return hipSuccess;
