@@ -27,6 +27,10 @@
 //  Tiles go from HBM straight into LDS (global_load_lds), two buffers, a quarter per wave, with
 //  the 16-byte-chunk swizzle chunk ^ (row / 2) % 8; both the row reads and the transposing reads
 //  of a tile use it.
+//  At d = 64 both gradient kernels run as ping-pong kernels (bwd_dq_pp, bwd_dkdv_pp): 8 waves
+//  in two groups in opposite matrix-core / softmax phases, as in the forward kernel, 256 rows
+//  (keys) per workgroup, three rotating tile buffers. The 4-wave kernels above serve d = 128,
+//  whose accumulators do not fit two waves per SIMD.
 
 #include "fa_internal.h"
 #include "mfma_common.h"
