@@ -142,3 +142,21 @@ def test_backward_headline_shape_sampled_heads():
         for name, got, ref in (("dq", dq[sl], rdq), ("dk", dk[sl], rdk), ("dv", dv[sl], rdv)):
             ma, rl = assert_grad_close(got, ref, "bf16", f"headline {name} head {(b, h)}")
             say(f"  head {(b, h)} {name}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+
+
+def test_backward_causal_workload_sampled_heads():
+    """The causal backward workload (B=4, H=16, N=4096, d=64 bf16, the causal mask; seed 3, dO = tensor 3),
+    the launch bench.py times: every head runs on the GPU (longest-first block order, all 16 key and
+    query tiles of each head); the oracle checks two heads in full."""
+    w = si.BWD_CAUSAL_BF16
+    q, k, v = si.workload_inputs(w)
+    do = si.grad_output(w)
+    say("bwd causal workload")
+    o, lse, dq, dk, dv, delta = run_gpu(q, k, v, do, w.scale, True)
+    for (b, h) in ((1, 4), (2, 11)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rdq, rdk, rdv, rlse, _ = oracle.attention_backward_fp64(q.as_f64()[sl], k.as_f64()[sl], v.as_f64()[sl],
+                                                                do.as_f64()[sl], w.scale, causal=True)
+        for name, got, ref in (("dq", dq[sl], rdq), ("dk", dk[sl], rdk), ("dv", dv[sl], rdv)):
+            ma, rl = assert_grad_close(got, ref, "bf16", f"causal workload {name} head {(b, h)}")
+            say(f"  head {(b, h)} {name}: max_abs={ma:.3e} rel_l2={rl:.3e}")
