@@ -237,14 +237,9 @@ __device__ __forceinline__ void pv_staged(const T* __restrict__ vfrag, const typ
     }
 }
 
-// Softmax update of one tile for one 32-query block, given the tile scores s (raw dot
-// products) of that block: moves the exponent reference when needed (scaling l and the block's
-// accumulator), writes P as PV operands and adds its row sum to l.
-//   FAST = false: exact running max, reference moves when the tile max exceeds it by > tau.
-//   FAST = true:  no running max; reference moves when the tile's row sum leaves [0, 2^tau].
-// Exponentials of one block's scores: p = 2^(s c2 - ref), 0 for masked (-inf) scores; returns
-// the row sum. At d = 64 the P operands are also rounded here (measured 1.5 % faster there; at
-// d = 128 rounding after the softmax update measured 2 % faster).
+// Exponentials of one block's scores: p = 2^(s c2 - ref), and with TAIL 0 for the keys at or
+// past the row's limit; returns the row sum. At d = 64 the P operands are also rounded here
+// (measured 1.5 % faster there; at d = 128 rounding after the softmax update measured 2 % faster).
 // Key index (within the tile, minus 4 hf) of value i = 16 kb + r of a 64-key block: key
 // 32 kb + 8 (r / 4) + 4 hf + r % 4 is masked when tail_key(i) >= limh = lim - 4 hf.
 __host__ __device__ constexpr int tail_key(int i) { return 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3); }
