@@ -679,6 +679,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
           if (a.l_out) a.l_out[head * a.Nq + row] = st.lsum[nb] * to_true;
           if (a.lse_out) a.lse_out[head * a.Nq + row] = a.scale * st.mraw[nb] + logf(st.lsum[nb] * to_true);
         }
+      } else {
+        // the log-sum-exp needs no maximum: sum_j e^(scale s_j) = 2^m2ref * lsum, whatever the
+        // reference (every term of lsum is at most 2^tau, so it carries full fp32 precision)
+        if (hf == 0 && a.lse_out)
+          a.lse_out[head * a.Nq + row] = st.m2ref[nb] * 0.6931471805599453f + logf(st.lsum[nb]);
       }
     } else if constexpr (!FAST) {
       // A row that saw no key of this range (causal mask) keeps the empty state (-inf, 0, 0).
@@ -716,9 +721,10 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
   int nq = n_qtiles;
   void* kargs[] = {&args, &nq};
-  // Full-output calls without row statistics take the sum-checked softmax; statistics, split
-  // states and a zero threshold (the literal recurrence) take the running-max form.
-  const bool fast = a.split_mode == 0 && !a.m_out && !a.l_out && !a.lse_out && a.rescale_threshold >= 1.f;
+  // Full-output calls without m / l take the sum-checked softmax (also with the log-sum-exp, which
+  // needs no maximum); m / l, split states and a zero threshold (the literal recurrence) take the
+  // running-max form.
+  const bool fast = a.split_mode == 0 && !a.m_out && !a.l_out && a.rescale_threshold >= 1.f;
   const void* k;
   if (a.causal) k = fast ? reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, true, true>)
                          : reinterpret_cast<const void*>(&fwd_mfma_kernel<D, T, false, true>);
