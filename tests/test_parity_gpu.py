@@ -436,3 +436,32 @@ def test_headline_bf16_full_size_no_stats():
         ref.append(oracle.attention_rows_fp64(qf[b, h, rows], kf[b, h], vf[b, h], w.scale)[0])
     say(f"headline no-stats errors {errors(np.concatenate(got), np.concatenate(ref))}")
     assert_close(np.concatenate(got), np.concatenate(ref), "bf16", "headline no-stats")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kmul,shift,ramp", [(1.0, 0.0, False), (8.0, 0.0, False), (1.0, 100.0, False),
+                                             (1.0, 0.0, True)])
+def test_lse_sum_checked_score_ranges(kmul, shift, ramp, causal):
+    """fa_fwd_lse takes the sum-checked softmax (lse = m_ref ln 2 + ln l for whatever reference the
+    row ended with): O and the log-sum-exp against the oracle's m + ln(l) on wide score ranges,
+    scores shifted to about 100, and scores growing tile after tile."""
+    q, k, v = si.small_case(79, 1, 2, 300, 1000, 64, "bf16", k_mult=kmul)
+    qf, kf = q.as_f64(), k.as_f64()
+    if shift:
+        u = qf[0, 0].mean(axis=0)
+        u = u * (shift / (0.125 * float(u @ u)))
+        kf = kf + u
+    if ramp:
+        kf = kf * np.linspace(0.1, 6.0, kf.shape[2])[None, None, :, None]
+    k = si.encode(kf.astype(np.float32), "bf16")
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    o, lse = fa.fwd_lse(qd, kd, vd, scale=0.125, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = si.torch_to_f64(o), si.torch_to_f64(lse)
+    ref, m_ref, l_ref = oracle.attention_fp64(qf, k.as_f64(), v.as_f64(), 0.125, return_stats=True, causal=causal)
+    what = f"lse kmul={kmul} shift={shift} ramp={ramp} causal={causal}"
+    assert_close(o, ref, "bf16", what)
+    # lse = m + ln(l): the bounds of m and of l's relative error (tests/_parity.py) add up
+    bound = 2 * stat_bound(qf, k.as_f64(), 0.125)
+    dl = np.abs(lse - (m_ref + np.log(l_ref)))
+    assert np.all(dl <= bound), f"{what}: lse off by {np.max(dl):.3e} (bound {np.min(bound):.1e}..)"
