@@ -24,9 +24,9 @@
 //  operands of the next 16-step MFMAs under the same fixed row permutation the forward kernel
 //  uses for P; the transposing reads follow it. P and dS are rounded to the input type (round to
 //  nearest even) only as MFMA operands; everything else is fp32.
-//  Tiles go from HBM straight into LDS (global_load_lds), two buffers, a quarter per wave, with
-//  the 16-byte-chunk swizzle chunk ^ (row / 2) % 8; both the row reads and the transposing reads
-//  of a tile use it.
+//  Tiles go from HBM straight into LDS (global_load_lds), a quarter per wave, with the 16-byte-
+//  chunk swizzle swz_rt, under which both the row reads and the transposing reads of a tile are
+//  free of bank conflicts.
 //  At d = 64 both gradient kernels run as ping-pong kernels (bwd_dq_pp, bwd_dkdv_pp): 8 waves
 //  in two groups in opposite matrix-core / softmax phases, as in the forward kernel, 256 rows
 //  (keys) per workgroup, three rotating tile buffers. The 4-wave kernels above serve d = 128,
@@ -63,7 +63,7 @@ __device__ __forceinline__ void global_to_lds4(const void* g, void* lds) {
 }
 
 // HBM -> LDS of a 64-row tile, a quarter per wave. LDS chunk c of tile row r holds global chunk
-// c ^ swzk(r); rows at or past `nrows` repeat row nrows - 1 (their results are masked or never
+// c ^ swz_rt<D>(r); rows at or past `nrows` repeat row nrows - 1 (their results are masked or never
 // stored).
 template <int D, typename T>
 __device__ __forceinline__ void load_tile(const T* __restrict__ X, T* lx, int row0, int nrows, int wave, int lane) {
@@ -74,7 +74,7 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ X, T* lx, int ro
     const int ci = base + lane;
     const int r = ci / C::CH, cpos = ci % C::CH;
     const int row = min(row0 + r, nrows - 1);
-    global_to_lds16(X + (size_t)row * D + ((cpos ^ swzk(r)) << 3), &lx[base * 8]);
+    global_to_lds16(X + (size_t)row * D + ((cpos ^ swz_rt<D>(r)) << 3), &lx[base * 8]);
   }
 }
 
@@ -86,7 +86,7 @@ __device__ __forceinline__ void load_rowvec(const float* __restrict__ x, float* 
 // 16 bytes of tile row r, global chunk ch: an A or B operand row fragment.
 template <int D, typename T>
 __device__ __forceinline__ typename Mma<T>::v8 row_frag(const T* lx, int r, int ch) {
-  return *reinterpret_cast<const typename Mma<T>::v8*>(&lx[r * D + ((ch ^ swzk(r)) << 3)]);
+  return *reinterpret_cast<const typename Mma<T>::v8*>(&lx[r * D + ((ch ^ swz_rt<D>(r)) << 3)]);
 }
 
 // A operand X^T[dims of block db][rows of 16-step g] of a row-major tile X, read transposed, in
@@ -100,8 +100,8 @@ __device__ __forceinline__ typename Mma<T>::v8 tr_frag(const T* lx, int g, int d
   const int tgb = (lane >> 4) & 1;
   const int row1 = 16 * g + 4 * hf + ti;
   const int col = db * 32 + tgb * 16 + tq * 4;
-  const int off1 = row1 * D + (((col >> 3) ^ swzk(row1)) << 3) + (col & 7);
-  const int off2 = (row1 + 8) * D + (((col >> 3) ^ swzk(row1 + 8)) << 3) + (col & 7);
+  const int off1 = row1 * D + (((col >> 3) ^ swz_rt<D>(row1)) << 3) + (col & 7);
+  const int off2 = (row1 + 8) * D + (((col >> 3) ^ swz_rt<D>(row1 + 8)) << 3) + (col & 7);
   const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off1]);
   const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off2]);
   const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
@@ -123,7 +123,7 @@ __device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[8]) {
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
 // This lane's byte offsets of the row_frag and tr_frag reads within a tile. The swizzle of a row
-// depends only on (row / 2) % 8, so a row read at row + 32 qb and a transposing read at rows
+// depends only on row % 16, so a row read at row + 32 qb and a transposing read at rows
 // + 16 g are these offsets plus a constant (64 qb D or 32 g D bytes), which the reads take as an
 // immediate. Kernels pass the offsets through an empty asm once per step, so the compiler cannot
 // hoist one register per (buffer, read) out of the loop.
@@ -134,14 +134,14 @@ struct LdsOff {
   __device__ __forceinline__ LdsOff(int lane) {
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) row[ks] = (unsigned)((l32 * D + (((ks * 2 + hf) ^ swzk(l32)) << 3)) * sizeof(T));
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = (unsigned)((l32 * D + (((ks * 2 + hf) ^ swz_rt<D>(l32)) << 3)) * sizeof(T));
     const int tj = lane & 15, ti = tj >> 2, tq = tj & 3, tgb = (lane >> 4) & 1;
     const int row1 = 4 * hf + ti;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int col = db * 32 + tgb * 16 + tq * 4;
-      tr1[db] = (unsigned)((row1 * D + (((col >> 3) ^ swzk(row1)) << 3) + (col & 7)) * sizeof(T));
-      tr2[db] = (unsigned)(((row1 + 8) * D + (((col >> 3) ^ swzk(row1 + 8)) << 3) + (col & 7)) * sizeof(T));
+      tr1[db] = (unsigned)((row1 * D + (((col >> 3) ^ swz_rt<D>(row1)) << 3) + (col & 7)) * sizeof(T));
+      tr2[db] = (unsigned)(((row1 + 8) * D + (((col >> 3) ^ swz_rt<D>(row1 + 8)) << 3) + (col & 7)) * sizeof(T));
     }
   }
   __device__ __forceinline__ void opaque() {
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
   for (int i = 0; i < C::LPW; ++i) {
     const int ci = (gw * C::LPW + i) * 64 + lane;
     const int r = ci / C::CH, cpos = ci % C::CH;
-    toff[i] = (unsigned)((r * D + ((cpos ^ swzk(r)) << 3)) * sizeof(T));
+    toff[i] = (unsigned)((r * D + ((cpos ^ swz_rt<D>(r)) << 3)) * sizeof(T));
   }
   auto tile_in = [&](const T* X, T* lx, int r0) __attribute__((always_inline)) {
     if (r0 + kTile <= a.Nq) {
@@ -903,7 +903,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dq_pp_kernel(BwdArgs a, 
   for (int i = 0; i < C::LPW; ++i) {
     const int ci = (gw * C::LPW + i) * 64 + lane;
     const int r = ci / C::CH, cpos = ci % C::CH;
-    toff[i] = (unsigned)((r * D + ((cpos ^ swzk(r)) << 3)) * sizeof(T));
+    toff[i] = (unsigned)((r * D + ((cpos ^ swz_rt<D>(r)) << 3)) * sizeof(T));
   }
   auto tile_in = [&](const T* X, T* lx, int k0) __attribute__((always_inline)) {
     if (k0 + kTile <= a.Nk) {

@@ -72,4 +72,24 @@ __device__ __forceinline__ void global_to_lds16(const void* g, void* lds) {
 __device__ __forceinline__ int swzk(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swzv(int r) { return ((r & 3) << 1); }
 
+// d = 128 (256-byte rows: every row spans all 64 banks): chunk c of row r at
+// c ^ (4 (r % 4) + (r / 4) % 4). Sixteen consecutive rows get sixteen different chunks, so a
+// 16-byte row read (16 lanes, 16 rows, one chunk column) meets no conflict; and the 32 lanes of
+// an 8-byte transposing read cover rows 4 i + j (j = 0..3) by 4 column chunks (2 bits) times
+// 2 halves of a chunk, and the swizzle moves row j's chunks by 4 j, into the two chunk bits the
+// columns leave free, so those lanes also hit 32 different bank pairs. (The forward kernel keeps
+// swzk / swzv at d = 128, which give both kinds of read two-way conflicts: there this swizzle
+// took the conflicts to zero, counted with SQ_LDS_BANK_CONFLICT, but measured 2 % slower.)
+__device__ __forceinline__ int swz128(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Tiles read both ways (rows and transposed; the backward kernels' Q, dO, K and V tiles). At
+// d = 64 the bits of (r >> 1) % 8 in reverse order: still a different chunk for each row pair of
+// 16 consecutive rows (row reads), and bit 1 of r, which tells the two row pairs of a
+// transposing read's 4-row group apart, lands in chunk bit 2, which its column chunks leave free
+// (swzk puts bit 3 there: a two-way conflict). At d = 128 swz128.
+template <int D>
+__device__ __forceinline__ int swz_rt(int r) {
+  return D == 128 ? swz128(r) : ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1));
+}
+
 }  // namespace fa
