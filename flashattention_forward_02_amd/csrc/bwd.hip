@@ -11,7 +11,8 @@
 // the causal mask the masked P_ij are 0.
 //
 // How it maps onto CDNA4. Three kernels, no atomics, every output written by one workgroup:
-//  * bwd_delta: D_i = sum_c dO_ic O_ic, one row per D/8 lanes.
+//  * bwd_delta: D_i = sum_c dO_ic O_ic, one row per D/8 lanes (at d = 64 the dQ kernel computes
+//    D itself).
 //  * bwd_dq: a workgroup owns 128 query rows of one (b, h) (32 per wave) and streams the head's
 //    K and V past them in 64-key tiles, exactly like the forward kernel: S^T = K Q^T and
 //    dP^T = V dO^T on 32x32x16 MFMAs with Q and dO held as B operands in registers, then in
@@ -885,7 +886,29 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dq_pp_kernel(BwdArgs a, 
     dof[ks] = *reinterpret_cast<const v8*>(dO + (size_t)rowc * D + ks * 16 + hf * 8);
   }
   const float L2 = a.lse[head * a.Nq + rowc] * kLog2e;
-  const float nDr = -a.delta[head * a.Nq + rowc];
+  // D_i = sum_c dO_ic O_ic of this lane's row, here rather than in a kernel of its own: the lane
+  // holds dims 16 ks + 8 hf .. + 7 of dO, the lane 32 apart the other half. Stored for the dK dV
+  // kernel, which runs after this one.
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const size_t e = (head * (size_t)a.Nq + rowc) * D + ks * 16 + hf * 8;
+    if (a.o_dtype == kF32) {
+      const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.o) + e);
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.o) + e + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsum = __builtin_fmaf((float)dof[ks][i], o0[i], dsum);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsum = __builtin_fmaf((float)dof[ks][4 + i], o1[i], dsum);
+    } else {
+      const v8 o = *reinterpret_cast<const v8*>(static_cast<const T*>(a.o) + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsum = __builtin_fmaf((float)dof[ks][i], (float)o[i], dsum);
+    }
+  }
+  dsum += __shfl_xor(dsum, 32);
+  if (hf == 0 && row < a.Nq) a.delta[head * a.Nq + row] = dsum;
+  const float nDr = -dsum;
   const float c2 = a.scale_log2e;
   const int last_key = CAUSAL ? row + a.causal_off : a.Nk - 1;   // keys past it are masked
   const int wave_last_key = CAUSAL ? min(qt * kPpOwn + wave * 32 + a.causal_off, a.Nk - 1) : a.Nk - 1;
@@ -1044,12 +1067,15 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const long long nk = (long long)n_ktiles * a.H_kv * a.B;
   if (nd > 0x7fffffffLL || nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   BwdArgs args = a;
-  if (rows > 0) {  // D first (the other two kernels read it), then dQ, then dK and dV
-    long long r = rows;
-    void* kargs[] = {&args, &r};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, T>), dim3((unsigned)nd),
-                                   dim3(256), kargs, 0, s);
-    if (e != hipSuccess) return e;
+  if (rows > 0) {  // D first (the other two kernels read it; at d = 64 the dQ kernel computes it), dQ, dK dV
+    hipError_t e = hipSuccess;
+    if constexpr (D != 64) {
+      long long r = rows;
+      void* kargs[] = {&args, &r};
+      e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<D, T>), dim3((unsigned)nd), dim3(256),
+                          kargs, 0, s);
+      if (e != hipSuccess) return e;
+    }
     if constexpr (D == 64) {  // ping-pong kernel: 256 query rows per workgroup
       int n = (a.Nq + kPpOwn - 1) / kPpOwn;
       const long long nqp = (long long)n * a.H * a.B;
