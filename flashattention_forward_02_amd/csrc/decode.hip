@@ -231,9 +231,176 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
   }
 }
 
+// R query rows of one head per workgroup (bf16 / fp16), so the rows share every K and V load:
+// the same lane layout and per-group recurrence as decode_kernel, with R scores per key and R
+// (m, l, o) states per group. Grouped K/V heads without the mask (or with one query row, which
+// sees every key) are run through it as one head of G * Nq rows per K/V head: query head
+// h = hk * G + g, row i is row g * Nq + i of K/V head hk, and [B, H, Nq] is [B, H_kv, G * Nq] in
+// memory, so the G query heads of a K/V head read K and V once instead of G times.
+template <int D, typename T, int U, int R>
+__global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
+  constexpr int DL = D / 16;  // columns per lane
+  __shared__ float sh_m[R][kGroups], sh_l[R][kGroups];
+  __shared__ float sh_o[R][kGroups][D];
+
+  const int S = a.num_splits;
+  const int n_blocks = (a.Nq + R - 1) / R;
+  const int split = blockIdx.x % S;
+  const int rest = blockIdx.x / S;
+  const int row0 = (rest % n_blocks) * R;
+  const size_t head = rest / n_blocks;     // heads share K/V (the caller's view is one-to-one)
+  const int kbeg = split_begin(split, a.Nk, S);
+  const int kend = split_begin(split + 1, a.Nk, S);
+
+  const int tid = threadIdx.x;
+  const int g = tid >> 4;
+  const int t = tid & 15;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + head * (size_t)a.Nk * D + t * DL;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + head * (size_t)a.Nk * D + t * DL;
+
+  float q[R][DL];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int row = min(row0 + j, a.Nq - 1);   // rows past Nq compute row Nq - 1 and are not stored
+    load_row<T, DL>(static_cast<const T*>(a.q) + (head * a.Nq + row) * (size_t)D + t * DL, q[j]);
+  }
+  const float c2 = a.scale_log2e;
+
+  float m[R], l[R], acc[R][DL];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) acc[j][c] = 0.f;
+  }
+
+  for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
+    float kx[U][DL], vx[U][DL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u;
+      if (key < kend) {
+        load_row<T, DL>(K + (size_t)key * D, kx[u]);
+        load_row<T, DL>(V + (size_t)key * D, vx[u]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;
+      }
+    }
+    float sc[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < DL; ++c) dot = __builtin_fmaf(q[j][c], kx[u][c], dot);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) dot += __shfl_xor(dot, off);
+        sc[u][j] = base + u < kend ? dot : -INFINITY;
+      }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
+      const float mnew = fmaxf(m[j], mx);
+      const float alpha = (m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[j] - mnew) * c2);
+      l[j] *= alpha;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) acc[j][c] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][j], c2, -mnew * c2));
+        if (sc[u][j] == -INFINITY) p = 0.f;
+        l[j] += p;
+#pragma unroll
+        for (int c = 0; c < DL; ++c) acc[j][c] = __builtin_fmaf(p, vx[u][c], acc[j][c]);
+      }
+      m[j] = mnew;
+    }
+  }
+
+  // ---- merge the 16 group states of each row (as in decode_kernel) ----
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (t == 0) {
+      sh_m[j][g] = m[j];
+      sh_l[j][g] = l[j];
+    }
+#pragma unroll
+    for (int c = 0; c < DL; ++c) sh_o[j][g][t * DL + c] = acc[j][c];
+  }
+  __syncthreads();
+  for (int j = 0; j < R; ++j) {
+    const int row = row0 + j;
+    if (row >= a.Nq) break;
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) M = fmaxf(M, sh_m[j][i]);
+    float w[kGroups];
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      const float mi = sh_m[j][i];
+      w[i] = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mi - M) * c2);
+      L = __builtin_fmaf(w[i], sh_l[j][i], L);
+    }
+    const float m_nat = (M == -INFINITY) ? M : a.scale * M;
+    const size_t qrow = head * a.Nq + row;
+    for (int c = tid; c < D; c += kThreads) {
+      float o = 0.f;
+#pragma unroll
+      for (int i = 0; i < kGroups; ++i) o = __builtin_fmaf(w[i], sh_o[j][i][c], o);
+      if (a.split_mode == 0) {
+        store_out<T>(a.o, qrow * D + c, a.out_dtype, o / L);
+      } else {
+        const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
+        a.part_o[prow * D + c] = (a.split_mode == 2) ? (L > 0.f ? o / L : 0.f) : o;
+      }
+    }
+    if (tid == 0) {
+      if (a.split_mode == 0) {
+        if (a.m_out) a.m_out[qrow] = m_nat;
+        if (a.l_out) a.l_out[qrow] = L;
+        if (a.lse_out) a.lse_out[qrow] = m_nat + logf(L);
+      } else {
+        const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
+        if (a.split_mode == 2) {
+          a.part_m[prow] = (M == -INFINITY) ? -INFINITY : m_nat + logf(L);
+        } else {
+          a.part_m[prow] = m_nat;
+          a.part_l[prow] = L;
+        }
+      }
+    }
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   constexpr int U = (D == 64) ? 8 : 4;
+  // Rows that share K and V go to decode_rows_kernel: without the mask (or with one row, which
+  // sees every key) the G * Nq rows of each K/V head, viewed as one head.
+  if constexpr (!std::is_same<T, float>::value) {
+    if (!a.causal || a.Nq == 1) {
+      FwdArgs v = a;
+      v.H = a.H_kv;
+      v.Nq = (a.H / a.H_kv) * a.Nq;
+      v.causal = 0;
+      if (v.Nq >= 2) {
+        const bool r4 = v.Nq >= 3;
+        const int R = r4 ? 4 : 2;
+        const long long nwg = (long long)a.num_splits * ((v.Nq + R - 1) / R) * v.H * v.B;
+        if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        void* kargs[] = {&v};
+        const void* k = r4 ? reinterpret_cast<const void*>(&decode_rows_kernel<D, T, U, 4>)
+                           : reinterpret_cast<const void*>(&decode_rows_kernel<D, T, U, 2>);
+        return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
+      }
+    }
+  }
   const long long nwg = (long long)a.num_splits * a.Nq * a.H * a.B;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
