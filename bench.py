@@ -248,7 +248,8 @@ def main():
                                   "Nk": wl.Nk, "d": wl.d, "num_splits": wl.num_splits,
                                   "merge_order": f"default_rng({wl.seed}).permutation({wl.num_splits})"}})
         achieved = alg_bytes / (split_ms * 1e-3) / 1e9
-        result["roofline"] = {"bound": "hbm", "kernel": "decode_kernel (split)", "achieved": achieved,
+        kname = "decode_rows_kernel (split)" if args.workload == "gqa_decode" else "decode_kernel (split)"
+        result["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                               **launch_stats, "traffic": traffic_for(args.workload, source_hash("decode.hip"))}
         if wl.dtype != "bf16":
