@@ -84,32 +84,6 @@ __device__ __forceinline__ void load_rowvec(const float* __restrict__ x, float* 
   global_to_lds4(x + min(row0 + lane, nrows - 1), lx);
 }
 
-// 16 bytes of tile row r, global chunk ch: an A or B operand row fragment.
-template <int D, typename T>
-__device__ __forceinline__ typename Mma<T>::v8 row_frag(const T* lx, int r, int ch) {
-  return *reinterpret_cast<const typename Mma<T>::v8*>(&lx[r * D + ((ch ^ swz_rt<D>(r)) << 3)]);
-}
-
-// A operand X^T[dims of block db][rows of 16-step g] of a row-major tile X, read transposed, in
-// the row order of the P operands built by pack8 (the forward kernel's V^T read).
-template <int D, typename T>
-__device__ __forceinline__ typename Mma<T>::v8 tr_frag(const T* lx, int g, int db, int lane) {
-  const int hf = lane >> 5;
-  const int tj = lane & 15;
-  const int ti = tj >> 2;
-  const int tq = tj & 3;
-  const int tgb = (lane >> 4) & 1;
-  const int row1 = 16 * g + 4 * hf + ti;
-  const int col = db * 32 + tgb * 16 + tq * 4;
-  const int off1 = row1 * D + (((col >> 3) ^ swz_rt<D>(row1)) << 3) + (col & 7);
-  const int off2 = (row1 + 8) * D + (((col >> 3) ^ swz_rt<D>(row1 + 8)) << 3) + (col & 7);
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off1]);
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)&lx[off2]);
-  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
-  const u32x4_t packed = {lo2[0], lo2[1], hi2[0], hi2[1]};
-  return __builtin_bit_cast(typename Mma<T>::v8, packed);
-}
-
 // Eight fp32 values rounded to T: one B operand of a 16-step (values i = 0..7 are registers
 // 8 (g % 2) + i of the accumulator block g / 2, the row order the transposing reads follow).
 template <typename T>
@@ -123,15 +97,21 @@ __device__ __forceinline__ typename Mma<T>::v8 pack8(const float (&x)[8]) {
 // Row index (within a 32-row block) of register r of lane half hf in a 32x32 accumulator.
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
-// This lane's byte offsets of the row_frag and tr_frag reads within a tile. The swizzle of a row
-// depends only on row % 16, so a row read at row + 32 qb and a transposing read at rows
-// + 16 g are these offsets plus a constant (64 qb D or 32 g D bytes), which the reads take as an
-// immediate. Kernels pass the offsets through an empty asm once per step, so the compiler cannot
-// hoist one register per (buffer, read) out of the loop.
+// This lane's byte offsets of its operand reads within a swizzled tile (LDS chunk c of row r holds
+// global chunk c ^ swz_rt<D>(r)):
+//  * row read: the 16 bytes of row l32, global chunk 2 ks + hf (an A or B operand row fragment);
+//  * transposing read: the A operand X^T[dims of 32-block db][rows of 16-step g] of a row-major
+//    tile X, in the row order of the P operands built by pack8 (the forward kernel's V^T read):
+//    two 8-byte ds_read_tr16_b64 at rows 16 g + 4 hf + (lane % 16) / 4 and 8 rows further, column
+//    32 db + 16 ((lane / 16) % 2) + 4 (lane % 4).
+// The swizzle of a row depends only on row % 16, so a row read at row + 32 qb and a transposing
+// read at rows + 16 g are these offsets plus a constant (64 qb D or 32 g D bytes), which the reads
+// take as an immediate. Kernels pass the offsets through an empty asm once per step, so the
+// compiler cannot hoist one register per (buffer, read) out of the loop.
 template <int D, typename T>
 struct LdsOff {
-  unsigned row[D / 16];                  // row_frag(lx, l32, 2 ks + hf)
-  unsigned tr1[D / 32], tr2[D / 32];     // tr_frag(lx, 0, db): the two 8-byte transposing reads
+  unsigned row[D / 16];                  // row read of row l32, chunk 2 ks + hf
+  unsigned tr1[D / 32], tr2[D / 32];     // the two 8-byte transposing reads of step g = 0, block db
   __device__ __forceinline__ LdsOff(int lane) {
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
@@ -152,13 +132,13 @@ struct LdsOff {
     for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(tr1[i]), "+v"(tr2[i]));
   }
 };
-// row_frag(lx, 32 qb + l32, 2 ks + hf) from the offsets
+// Row read of row 32 qb + l32, chunk 2 ks + hf
 template <int D, typename T>
 __device__ __forceinline__ typename Mma<T>::v8 row_frag_o(const T* lx, const LdsOff<D, T>& o, int qb, int ks) {
   const char* p = reinterpret_cast<const char*>(lx) + o.row[ks] + qb * 32 * D * (int)sizeof(T);
   return *reinterpret_cast<const typename Mma<T>::v8*>(p);
 }
-// tr_frag(lx, g, db, lane) from the offsets
+// Transposing read of 16-row step g, 32-dim block db
 template <int D, typename T>
 __device__ __forceinline__ typename Mma<T>::v8 tr_frag_o(const T* lx, const LdsOff<D, T>& o, int g, int db) {
   const char* base = reinterpret_cast<const char*>(lx) + g * 16 * D * (int)sizeof(T);
