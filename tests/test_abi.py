@@ -1,6 +1,5 @@
 """The C ABI without a GPU: the library loads, exports every declared entry point, and rejects bad
 arguments with the documented status before touching the device (CPU only; no compute calls)."""
-import ctypes
 import os
 import re
 import subprocess

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from tests._parity import BWD_TOL, assert_grad_close, stat_bound, errors
+from tests._parity import assert_grad_close, stat_bound
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu

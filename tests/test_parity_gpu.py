@@ -3,7 +3,6 @@
 Tolerances live in tests/_parity.py. Small cases span several tiles and ragged tails; the
 workload-size cases compare sampled rows that the oracle computes one head at a time.
 """
-import math
 import sys
 
 import numpy as np
