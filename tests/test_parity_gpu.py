@@ -70,6 +70,35 @@ def test_small_shapes(dtype, shape):
     assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), scale), f"{dtype} {shape}")
 
 
+# Key-tile counts 1, 2 and 3 (full and ragged), with and without the causal mask and the row
+# statistics (without them the tiled kernel takes its sum-checked path): the d = 64 tiled kernel
+# synchronises once per 64-key tile, the d = 128 one twice, and the first and last tiles and the
+# prologue differ between the two wave groups.
+TILE_COUNTS = [(100, nk, False) for nk in (1, 33, 64, 65, 128, 129, 192)] + \
+    [(17, 17, True), (64, 64, True), (65, 65, True), (100, 129, True), (130, 130, True), (64, 192, True)]
+
+
+@pytest.mark.parametrize("stats", [False, True], ids=["fast", "stats"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", TILE_COUNTS, ids=lambda c: f"{c[0]}x{c[1]}{'c' if c[2] else ''}")
+def test_key_tile_counts(case, d, stats):
+    Nq, Nk, causal = case
+    say(f"key tile counts Nq={Nq} Nk={Nk} d={d} causal={causal} stats={stats}")
+    q, k, v = si.small_case(3000 + Nq + Nk + d, 1, 2, Nq, Nk, d, "bf16")
+    scale = si.fp32_inverse_sqrt(d)
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    res = fa.fwd(qd, kd, vd, scale=scale, out_dtype=torch.float32, return_stats=stats, causal=causal)
+    torch.cuda.synchronize()
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale, return_stats=True,
+                                              causal=causal)
+    if stats:
+        o, m, l = (si.torch_to_f64(x) for x in res)
+        assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), scale), f"tiles {case} d={d}")
+    else:
+        o = si.torch_to_f64(res)
+    assert_close(o, ref, "bf16", f"tiles {case} d={d} stats={stats}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_low_precision_output_dtype(dtype):
     q, k, v = si.small_case(77, 2, 2, 300, 500, 64, dtype)
