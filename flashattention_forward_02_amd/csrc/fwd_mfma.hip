@@ -14,9 +14,10 @@
 //    overlap at all). A workgroup therefore has 8 waves, two per SIMD: group A (waves 0-3)
 //    and group B (waves 4-7), each owning its own query rows. Every tile is two phases per
 //    wave -- an MFMA phase (PV of the previous tile, then S of this tile) and a VALU phase
-//    (the softmax update of this tile) -- and group B runs one phase behind group A, with a
-//    workgroup barrier between phases. So at any time one wave of each SIMD is on the matrix
-//    core while the other is on the VALU.
+//    (the softmax update of this tile) -- and group B runs one phase behind group A, held there
+//    by workgroup barriers (at d = 128 one after every phase; at d = 64 one per tile, A's after
+//    its VALU phase and B's after its MFMA phase). So at any time one wave of each SIMD is on
+//    the matrix core while the other is on the VALU.
 //  * Transposed products. S^T = K Q^T and O^T = V^T P^T, each as 32x32x16 MFMAs. In the
 //    32x32 accumulator layout a lane owns one column and 16 rows; with queries as columns a
 //    lane holds 16 scores of ONE query (rows = keys) and 16 output dims of that same query.
