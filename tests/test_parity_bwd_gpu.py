@@ -76,6 +76,10 @@ CASES = [
     (1, 4, 2, 200, 200, 128, True),
     (1, 2, 2, 7, 7, 128, True),
     (1, 8, 1, 70, 260, 64, False),
+    # whole tiles: 1, 2 and 3 query or key tiles (the ping-pong kernels' steps rotate three buffers)
+    (1, 2, 2, 64, 64, 64, False),
+    (1, 2, 2, 128, 192, 64, True),
+    (1, 1, 1, 192, 128, 64, False),
 ]
 
 
