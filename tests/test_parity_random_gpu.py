@@ -1,0 +1,84 @@
+"""GPU parity on seeded random shapes: forward (with and without row statistics), split-KV in both
+state forms with a shuffled merge, and the backward pass, against the fp64 oracle.
+
+Each case draws (B, H, H_kv, Nq, Nk, d, causal, dtype) from its own seeded generator, so a failure
+names a case that reruns alone. Sizes stay small enough for the oracle to finish in well under a
+second; the fixed-shape tests cover the workload sizes.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from tests._parity import assert_close, assert_grad_close, assert_stats, stat_bound
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import flashattention_forward_02_amd as fa
+    from tests import test_parity_bwd_gpu as bw
+    from tests import test_parity_causal_gqa_gpu as gq
+
+DEV = "cuda:0"
+N_CASES = 120
+
+
+def draw(i):
+    r = random.Random(90210 + i)
+    kind = r.choice(["fwd", "fwd", "split", "bwd"])
+    d = r.choice([64, 128])
+    H_kv = r.choice([1, 2])
+    H = H_kv * r.choice([1, 2, 4])
+    B = r.choice([1, 2])
+    causal = r.random() < 0.5
+    Nq, Nk = r.randint(1, 700), r.randint(1, 700)
+    if kind == "bwd":
+        Nq, Nk = min(Nq, 400), min(Nk, 400)
+    if causal:
+        Nq = min(Nq, Nk)
+    dtype = r.choice(["bf16", "f16"] + (["f32"] if kind != "bwd" else []))
+    return dict(kind=kind, B=B, H=H, H_kv=H_kv, Nq=Nq, Nk=Nk, d=d, causal=causal, dtype=dtype,
+                stats=r.random() < 0.5, splits=r.randint(1, min(Nk, 40)), lse_form=r.random() < 0.5,
+                seed=r.randint(0, 10 ** 6))
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    c = draw(i)
+    print(f"random case {i}: {c}", flush=True)
+    B, H, H_kv, Nq, Nk, d, dtype, causal = (c[x] for x in ("B", "H", "H_kv", "Nq", "Nk", "d", "dtype", "causal"))
+    scale = si.fp32_inverse_sqrt(d)
+    if c["kind"] == "bwd":
+        q, k, v, do = bw.case(c["seed"], B, H, H_kv, Nq, Nk, d, dtype)
+        o, lse, dq, dk, dv, delta = bw.run_gpu(q, k, v, do, scale, causal)
+        rdq, rdk, rdv, rlse, _ = oracle.attention_backward_fp64(q.as_f64(), k.as_f64(), v.as_f64(), do.as_f64(),
+                                                                scale, causal=causal)
+        bound = stat_bound(q.as_f64(), np.repeat(k.as_f64(), H // H_kv, axis=1), scale)
+        assert np.all(np.abs(lse - rlse) <= bound), f"lse off by {np.max(np.abs(lse - rlse)):.3e}"
+        zb = bw.zero_bounds(q, k, v, do, H // H_kv, scale)
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad_close(got, ref, dtype, f"case {i} {name}", zero_bound=zb.get(name))
+        return
+    q, k, v = gq.grouped_case(c["seed"], B, H, H_kv, Nq, Nk, d, dtype)
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale, return_stats=True,
+                                              causal=causal)
+    if c["kind"] == "fwd":
+        o, m, l = gq.run(q, k, v, scale, causal, c["stats"])
+        assert_close(o, ref, dtype, f"case {i}")
+        if c["stats"]:
+            assert_stats(m, l, m_ref, l_ref, gq.bound_for(q, k, H, scale), f"case {i}")
+        return
+    S = c["splits"]
+    order = si.merge_order(c["seed"], S)
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    if c["lse_form"]:
+        pl, po = fa.fwd_split_lse(qd, kd, vd, S, scale=scale, causal=causal)
+        o = fa.merge_lse(pl, po, order=order, return_lse=False)
+    else:
+        pm, pl, po = fa.fwd_split(qd, kd, vd, S, scale=scale, causal=causal)
+        o = fa.merge_states(pm, pl, po, order=order)
+    torch.cuda.synchronize()
+    assert_close(si.torch_to_f64(o), ref, dtype, f"case {i} splits={S}")
