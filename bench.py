@@ -1,16 +1,31 @@
 """Benchmark of the FlashAttention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload headline|headline_f16|long_seq|causal|decode|decode_lse|gqa_decode|bwd|bwd_causal]
-                    [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s SECONDS] [--workload NAME]
+                    [--no-cpu] [--no-probe]
 
-A step is one forward over the whole batch (headline, headline_f16, long_seq, causal), one split +
-merge pair (decode, gqa_decode; decode_lse with the states in the (lse, o) form), or one backward
-call over the whole batch (bwd, bwd_causal: dQ, dK, dV from the stored log-sum-exp; the forward
-that produces O and it runs once before the timed region). Inputs are generated and resident in
-HBM before the timed region. Prints ONE JSON line. The default workload is B=4, H=16, N=4096,
-d=64, bf16 (TFLOP/s = 4*B*H*N^2*d / time per step); the causal workloads count 4*d (forward) or
-10*d (backward) flops per visible (query, key) pair.
+Workloads (one step = one call over the whole batch, inputs resident in HBM before timing):
+
+    headline          forward, B=4 H=16 N=4096 d=64 bf16 (the default line)
+    headline_f16      the same in fp16
+    headline_literal  the headline with the literal recurrence: exact running max, l and acc
+                      rescaled by exp(m_old - m_new) whenever the maximum grows
+    long_seq          forward, B=1 H=32 N=16384 d=128 bf16, K x3
+    causal            the headline shape under the causal mask (4*d flops per visible pair)
+    single_head       forward, B=H=1 N=256 d=64 fp32 (latency-bound; reported in microseconds)
+    one_query         one query of d=64 against 4096 keys, fp32 (microseconds)
+    batched_queries   4096 queries sharing those 4096 keys, fp32 (TFLOP/s against the fp32 peak)
+    decode, decode_lse, gqa_decode
+                      split-KV decode (16 ranges) + merge; (m, l, o) or (lse, o) states; GB/s
+    bwd, bwd_causal, bwd_d128
+                      fa_bwd at the headline shape / under the mask / at d=128 (10*d flops per pair)
+
+Before the W warm-up steps, steps run back to back for --prewarm-s seconds (reported under
+"prewarm"): the GPU's clock ramps up under sustained load, and a short run would otherwise time a
+cold chip. The shader clock (amdsmi) is sampled around the timed region. After the timed region the
+two probes of include/fa_probe.h measure the matrix-core and HBM-read ceilings of the same GPU in the
+same process ("probe"; roofline.frac_of_probe). The cpu_baseline leg times the fp64 oracle on a
+bounded sample of the same inputs in a pool of worker processes on the host's cores.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -18,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,8 +41,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # published fp32 vector peak (counts packed fp32 FMAs)
 HBM_PEAK_GBS = 8000.0
 METRIC = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 bf16; % of MFMA peak"
+
+FWD_WORKLOADS = ("headline", "headline_f16", "headline_literal", "long_seq", "causal", "single_head", "one_query",
+                 "batched_queries")
+DECODE_WORKLOADS = ("decode", "decode_lse", "gqa_decode")
+BWD_WORKLOADS = ("bwd", "bwd_causal", "bwd_d128")
 
 
 def parse():
@@ -34,95 +56,222 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="headline",
-                   choices=["headline", "headline_f16", "long_seq", "causal", "decode", "decode_lse", "gqa_decode",
-                            "bwd", "bwd_causal"])
+    p.add_argument("--prewarm-s", type=float, default=2.0,
+                   help="seconds of back-to-back steps before the warm-up steps (clock ramp); 0 to skip")
+    p.add_argument("--workload", default="headline", choices=FWD_WORKLOADS + DECODE_WORKLOADS + BWD_WORKLOADS)
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--no-probe", action="store_true", help="skip the matrix-core and HBM probes")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0, help="wall-time budget of the cpu_baseline leg")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before warm-up, run one plain device copy of MIB MiB (reads MIB, writes MIB): the "
                         "reference dispatch that scales the HBM byte counters of a profiling run")
     return p.parse_args()
 
 
-def source_hash(*names):
+# ---------------------------------------------------------------------------
+# evidence records
+# ---------------------------------------------------------------------------
+
+def device_code_hash(*names):
+    """Hash of the device code a kernel is built from: the named sources plus the internal headers, with
+    comments and blank space removed, so that a comment-only edit keeps the hash and any code edit changes it."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "flashattention_forward_02_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "flashattention_forward_02_amd", "csrc")
+    for n in tuple(names) + ("fa_internal.h", "mfma_common.h"):
+        text = open(os.path.join(csrc, n), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(n.encode() + b"\0" + text.encode() + b"\0")
     return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_key, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on this exact source."""
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on this exact device code."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel_key)
-    if not rec or rec.get("source_hash") != src_hash:
+    if not rec or rec.get("device_code_hash") != src_hash:
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, o_gpu, max_heads):
-    """Time the fp64 oracle on a bounded sample of the same workload (whole heads), on this host's cores."""
-    import numpy as np
-    import oracle
-    import seeded_inputs as si
-    from threadpoolctl import threadpool_info
+class GfxClock:
+    """Current shader (GFX) clock of the GPU behind cuda:0, read through amdsmi; None when unavailable."""
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
-    errs = []
+    def __init__(self, torch):
+        self.h = None
+        self.err = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            try:
+                pr = torch.cuda.get_device_properties(0)
+                want = (int(getattr(pr, "pci_domain_id", 0)), int(pr.pci_bus_id), int(pr.pci_device_id))
+            except Exception:
+                pass
+            for hd in handles:
+                if want is None:
+                    break
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(hd)        # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.h = hd
+            if self.h is None and len(handles) == 1:
+                self.h = handles[0]
+            self.amdsmi = amdsmi
+        except Exception as e:  # no amdsmi, no permission: the figure is reported as null
+            self.err = repr(e)[:200]
+
+    def read(self):
+        if self.h is None:
+            return None
+        try:
+            return int(self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)["clk"])
+        except Exception:
+            return None
+
+
+def cpu_model():
+    try:
+        out = os.popen("lscpu 2>/dev/null").read()
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
+# ---------------------------------------------------------------------------
+# cpu_baseline: the fp64 oracle in a pool of worker processes
+# ---------------------------------------------------------------------------
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)           # one BLAS thread per worker process
+    global _ORACLE
+    import oracle as _o
+    _ORACLE = _o
+
+
+def _oracle_task(task):
+    """One task of the cpu_baseline leg: oracle rows r0..r1 of one head (forward) or one whole head (backward)."""
+    import numpy as np
+    kind, key, arrays, scale, causal = task
     t0 = time.perf_counter()
-    done = 0
-    for (b, h) in heads:
-        qh, kh, vh = (si.torch_to_f64(x[b, h]) for x in (q, k, v))
-        ref = oracle.attention_fp64(qh[None], kh[None], vh[None], w.scale)[0]
-        got = si.torch_to_f64(o_gpu[b, h])
-        errs.append((float(np.max(np.abs(got - ref))), float(np.linalg.norm(got - ref)), float(np.linalg.norm(ref))))
-        done += 1
-        if time.perf_counter() - t0 > 25.0:
-            break
-    dt = time.perf_counter() - t0
-    flops = 4.0 * done * w.Nq * w.Nk * w.d
+    if kind == "fwd":
+        q, k, v, r0, Nq = arrays
+        last = None
+        if causal:
+            last = _ORACLE.causal_last_key(np.arange(r0, r0 + q.shape[0]), Nq, k.shape[0])
+        ref = _ORACLE.attention_rows_fp64(q, k, v, scale, last_key=last)[0]
+    else:
+        q, k, v, do = arrays
+        ref = _ORACLE.attention_backward_fp64(q[None, None], k[None, None], v[None, None], do[None, None], scale,
+                                              causal=causal)[:3]
+    return key, ref, time.perf_counter() - t0
+
+
+def cpu_baseline(tasks, flops_of, budget_s, compare):
+    """Run oracle tasks in a process pool for at most ``budget_s`` seconds of wall time (after the workers
+    start). Returns (cpu_baseline record, parity record)."""
+    import multiprocessing as mp
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+    ctx = mp.get_context("spawn")      # fresh interpreters: nothing of this process's GPU state is inherited
+    pool = ctx.Pool(workers, initializer=_worker_init)
+    try:
+        pool.map(abs, range(workers))  # workers up and oracle imported before the clock starts
+        t0 = time.perf_counter()
+        done, flops, errs = 0, 0.0, []
+        for key, ref, _ in pool.imap_unordered(_oracle_task, tasks):
+            done += 1
+            flops += flops_of(key)
+            errs.extend(compare(key, ref))
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        pool.terminate()
+        pool.join()
     max_abs = max(e[0] for e in errs)
-    rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / (sum(e[2] ** 2 for e in errs) ** 0.5)
-    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-             "sample": f"{done} of {w.B * w.H} heads (all {w.Nq} query rows each) of the same inputs, "
-                       f"{dt:.1f} s wall, fp64 numpy"},
-            {"max_abs": max_abs, "rel_l2": rel, "heads_checked": done})
+    rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / max(sum(e[2] ** 2 for e in errs) ** 0.5, 1e-300)
+    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "cpu_model": cpu_model(),
+             "host_cpus": os.cpu_count(), "kind": "oracle", "wall_s": dt, "tasks_done": done,
+             "tasks_total": len(tasks)},
+            {"max_abs": max_abs, "rel_l2": rel, "tasks_checked": done})
 
 
-def cpu_baseline_bwd(w, q, k, v, do, grads, max_heads):
-    """Time the fp64 gradient oracle on a bounded sample of whole heads of the same workload, on this host."""
-    import numpy as np
-    import oracle
+def fwd_oracle_tasks(w, q, k, v, rows_per_task):
     import seeded_inputs as si
-    from threadpoolctl import threadpool_info
+    tasks = []
+    for b in range(w.B):
+        for h in range(w.H):
+            hk = h // (w.H // w.kv_heads)
+            kh, vh = si.torch_to_f64(k[b, hk]), si.torch_to_f64(v[b, hk])
+            qh = si.torch_to_f64(q[b, h])
+            for r0 in range(0, w.Nq, rows_per_task):
+                r1 = min(w.Nq, r0 + rows_per_task)
+                tasks.append(("fwd", (b, h, r0, r1), (qh[r0:r1], kh, vh, r0, w.Nq), w.scale, w.causal))
+    return tasks
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
-    errs = []
-    t0 = time.perf_counter()
-    done = 0
-    for (b, h) in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.attention_backward_fp64(*(si.torch_to_f64(x[sl]) for x in (q, k, v, do)), w.scale,
-                                             causal=w.causal)[:3]
-        for g, r in zip(grads, ref):
-            got = si.torch_to_f64(g[sl])
-            errs.append((float(np.max(np.abs(got - r))), float(np.linalg.norm(got - r)), float(np.linalg.norm(r))))
-        done += 1
-        if time.perf_counter() - t0 > 20.0:
-            break
-    dt = time.perf_counter() - t0
-    flops = 10.0 * done * w.visible_pairs * w.d
-    rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / (sum(e[2] ** 2 for e in errs) ** 0.5)
-    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-             "sample": f"{done} of {w.B * w.H} heads (dQ, dK, dV of all {w.Nq} rows) of the same inputs, "
-                       f"{dt:.1f} s wall, fp64 numpy"},
-            {"max_abs": max(e[0] for e in errs), "rel_l2": rel, "heads_checked": done})
 
+def err_triplet(got, ref):
+    import numpy as np
+    return (float(np.max(np.abs(got - ref))), float(np.linalg.norm(got - ref)), float(np.linalg.norm(ref)))
+
+
+# ---------------------------------------------------------------------------
+# probes
+# ---------------------------------------------------------------------------
+
+def run_probes(torch, fa, stream):
+    """Matrix-core and HBM-read ceilings of this GPU (include/fa_probe.h), best of 5 timed launches each."""
+    res = {}
+    flops, out = fa.probe_mfma_bf16(nblocks=2048, iters=1024)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fa.probe_mfma_bf16(nblocks=2048, iters=1024, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    res["mfma_bf16_tflops"] = flops / (best * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    rout = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    nbytes = fa.probe_hbm_read(buf, nblocks=4096, out=rout)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fa.probe_hbm_read(buf, nblocks=4096, out=rout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    res["hbm_read_gbs"] = nbytes / (best * 1e-3) / 1e9
+    res["what"] = ("fa_probe_mfma_bf16 (2048 workgroups x 4 waves x 1024 x 8 MFMAs 32x32x16) and fa_probe_hbm_read "
+                   "(4 GiB, 16-byte loads), best of 5 launches each")
+    del buf
+    return res
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
 
 def main():
     args = parse()
@@ -130,6 +279,11 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not implemented "
                                    "(heads shard across GPUs with no exchange; see the design notes)"}))
         sys.exit(2)
+    wname = args.workload
+    if wname == "headline_literal":
+        # rescale l and acc by 2^(m_ref_old - m_ref_new) whenever the running maximum grows (read once, at the
+        # library's first call)
+        os.environ["FA_RESCALE_THRESHOLD"] = "0"
 
     import torch
     import flashattention_forward_02_amd as fa
@@ -137,18 +291,25 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    wl = {"headline": si.HEADLINE_BF16, "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16,
-          "decode": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16, "bwd": si.BWD_BF16,
-          "bwd_causal": si.BWD_CAUSAL_BF16,
-          "headline_f16": si.HEADLINE_F16, "decode_lse": si.DECODE_BF16}[args.workload]
-    is_bwd = args.workload in ("bwd", "bwd_causal")
-    is_decode = args.workload in ("decode", "gqa_decode", "decode_lse")
-    lse_form = args.workload == "decode_lse"
+    wl = {"headline": si.HEADLINE_BF16, "headline_f16": si.HEADLINE_F16, "headline_literal": si.HEADLINE_BF16,
+          "long_seq": si.LONG_SEQ_BF16, "causal": si.CAUSAL_BF16, "single_head": si.SINGLE_HEAD_FP32,
+          "one_query": si.ONE_QUERY_LONG_KEYS, "batched_queries": si.BATCHED_QUERIES_LONG_KEYS,
+          "decode": si.DECODE_BF16, "decode_lse": si.DECODE_BF16, "gqa_decode": si.GQA_DECODE_BF16,
+          "bwd": si.BWD_BF16, "bwd_causal": si.BWD_CAUSAL_BF16, "bwd_d128": si.BWD_D128_BF16}[wname]
+    is_bwd = wname in BWD_WORKLOADS
+    is_decode = wname in DECODE_WORKLOADS
+    lse_form = wname == "decode_lse"
+    clock = GfxClock(torch)
 
     if is_decode:
         q, k, v = si.decode_inputs_device(wl, dev)
     else:
-        qh, kh, vh = si.workload_inputs(wl)
+        if wname == "single_head":
+            qh, kh, vh = si.single_head_fp32()
+        elif wname in ("one_query", "batched_queries"):
+            qh, kh, vh = si.one_query_long_keys(batched=wname == "batched_queries")
+        else:
+            qh, kh, vh = si.workload_inputs(wl)
         q, k, v = qh.to_torch(dev), kh.to_torch(dev), vh.to_torch(dev)
         del qh, kh, vh
         if is_bwd:
@@ -208,9 +369,27 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
+    # pre-warm: back-to-back steps for a fixed wall time (the clock ramps up under load)
+    clk_idle = clock.read()
+    prewarm_steps, clk_prewarm = 0, []
+    t_pw = time.perf_counter()
+    if args.prewarm_s > 0:
+        step()
+        torch.cuda.synchronize()
+        while time.perf_counter() - t_pw < args.prewarm_s:
+            for _ in range(8):
+                step()
+            prewarm_steps += 8
+            torch.cuda.synchronize()
+            if prewarm_steps % 256 == 0:
+                clk_prewarm.append(clock.read())
+        prewarm_steps += 1
+    prewarm_wall = time.perf_counter() - t_pw
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    clk_before = clock.read()
 
     # timed region: exactly K steps, synchronised on both sides
     ev_start = torch.cuda.Event(enable_timing=True)
@@ -225,6 +404,7 @@ def main():
     ev_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clk_after = clock.read()
     gpu_ms = ev_start.elapsed_time(ev_end)
     ms_per_step = gpu_ms / args.steps
     launch_ms = sorted(a.elapsed_time(b) for a, b in kev)
@@ -235,6 +415,8 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) draws, see seeded_inputs)"}
+    if wl.dtype != "bf16":
+        result["dtype"] = {"f16": "fp16", "f32": "fp32"}[wl.dtype]
     if is_decode:
         split_ms = avg_launch_ms
         kv_bytes = 2.0 * wl.B * wl.kv_heads * wl.Nk * wl.d * 2
@@ -248,56 +430,116 @@ def main():
                                   "Nk": wl.Nk, "d": wl.d, "num_splits": wl.num_splits,
                                   "merge_order": f"default_rng({wl.seed}).permutation({wl.num_splits})"}})
         achieved = alg_bytes / (split_ms * 1e-3) / 1e9
-        kname = "decode_rows_kernel (split)" if args.workload == "gqa_decode" else "decode_kernel (split)"
+        kname = "decode_rows_kernel (split)" if wname == "gqa_decode" else "decode_kernel (split)"
         result["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                              **launch_stats, "traffic": traffic_for(args.workload, source_hash("decode.hip"))}
-        if wl.dtype != "bf16":
-            result["dtype"] = wl.dtype
+                              **launch_stats, "traffic": traffic_for(wname, device_code_hash("decode.hip"))}
         result["step_bytes"] = step_bytes
     elif is_bwd:
         flops = 2.5 * wl.flops   # 10*d per visible pair: the products S, dP, dV, dK, dQ
-        metric = ("FA bwd TFLOP/s (10*B*H*N^2*d: the products S, dP, dV, dK, dQ) at N=4096,d=64 bf16; "
-                  "% of MFMA peak")
+        shape = f"N={wl.Nq},d={wl.d} bf16"
+        metric = f"FA bwd TFLOP/s (10*B*H*N^2*d: the products S, dP, dV, dK, dQ) at {shape}; % of MFMA peak"
         if wl.causal:
-            metric = ("FA bwd causal TFLOP/s (10*d per visible query-key pair, B*H*N(N+1)/2 pairs) at "
-                      "N=4096,d=64 bf16; % of MFMA peak")
+            metric = (f"FA bwd causal TFLOP/s (10*d per visible query-key pair, B*H*N(N+1)/2 pairs) at {shape}; "
+                      "% of MFMA peak")
         result.update({"metric": metric, "unit": "TFLOP/s",
                        "value": flops / (ms_per_step * 1e-3) / 1e12,
                        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
                                   "causal": wl.causal, "grad_dtype": "fp32"}})
         achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-        result["roofline"] = {"bound": "mfma", "kernel": "fa_bwd (bwd_dq_pp + bwd_dkdv_pp)",
-                              "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
-                              "traffic": traffic_for(args.workload, source_hash("bwd.hip"))}
+        kname = "fa_bwd (bwd_dq_pp + bwd_dkdv_pp)" if wl.d == 64 else "fa_bwd (bwd_delta + bwd_dq + bwd_dkdv)"
+        result["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
+                              "traffic": traffic_for(wname, device_code_hash("bwd.hip"))}
     else:
         flops = wl.flops
         tflops = flops / (ms_per_step * 1e-3) / 1e12
-        if args.workload == "long_seq":
-            result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=16384,d=128 bf16, K x3; % of MFMA peak"
-        if args.workload == "headline_f16":
-            result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 fp16; % of MFMA peak"
-            result["dtype"] = "fp16"
-        if args.workload == "causal":
-            result["metric"] = ("FA fwd causal TFLOP/s (4*d per visible query-key pair, B*H*N(N+1)/2 pairs) "
-                                "at N=4096,d=64 bf16; % of MFMA peak")
-        result.update({"unit": "TFLOP/s", "value": tflops,
-                       "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
-                                  "causal": wl.causal, "out_dtype": "fp32"}})
         achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-        result["roofline"] = {"bound": "mfma", "kernel": "fwd_mfma_kernel", "achieved": achieved,
-                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
-                              "traffic": traffic_for(args.workload, source_hash("fwd_mfma.hip"))}
+        cfg = {"workload": wl.name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "Nk": wl.Nk, "d": wl.d, "causal": wl.causal,
+               "out_dtype": "fp32"}
+        if wname in ("single_head", "one_query"):
+            # latency-bound correctness shapes: the figure is the time per call
+            what = ("B=H=1,N=256,d=64 fp32" if wname == "single_head"
+                    else "one query, Nk=4096, d=64 fp32, keys in blocks of 256 in the pages' demo")
+            result.update({"metric": f"FA fwd microseconds per call at {what}", "unit": "us",
+                           "value": ms_per_step * 1e3, "higher_is_better": False, "config": cfg,
+                           "tflops": tflops})
+            kname = "decode_kernel" if wname == "one_query" else "fwd_f32_kernel"
+            result["roofline"] = {"bound": "alu", "kernel": kname, "achieved": achieved,
+                                  "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, **launch_stats, "traffic": None}
+        elif wname == "batched_queries":
+            result.update({"metric": "FA fwd TFLOP/s (4*Nq*Nk*d) at 4096 queries sharing Nk=4096 keys, d=64 fp32; "
+                                     "% of fp32 vector peak", "unit": "TFLOP/s", "value": tflops, "config": cfg})
+            result["roofline"] = {"bound": "alu", "kernel": "fwd_f32_kernel", "achieved": achieved,
+                                  "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, **launch_stats, "traffic": None}
+        else:
+            if wname == "long_seq":
+                result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=16384,d=128 bf16, K x3; % of MFMA peak"
+            if wname == "headline_f16":
+                result["metric"] = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 fp16; % of MFMA peak"
+            if wname == "headline_literal":
+                result["metric"] = ("FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 bf16, literal recurrence (exact "
+                                    "running max, rescale on every increase); % of MFMA peak")
+            if wname == "causal":
+                result["metric"] = ("FA fwd causal TFLOP/s (4*d per visible query-key pair, B*H*N(N+1)/2 pairs) "
+                                    "at N=4096,d=64 bf16; % of MFMA peak")
+            result.update({"unit": "TFLOP/s", "value": tflops, "config": cfg})
+            result["roofline"] = {"bound": "mfma", "kernel": "fwd_mfma_kernel", "achieved": achieved,
+                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
+                                  "traffic": traffic_for(wname, device_code_hash("fwd_mfma.hip"))}
+    result["prewarm"] = {"seconds": prewarm_wall, "steps": prewarm_steps}
+    result["sclk_mhz"] = {"idle": clk_idle, "prewarm": clk_prewarm[-8:], "before_timed": clk_before,
+                          "after_timed": clk_after, "source": "amdsmi GFX clock" if clock.h is not None
+                          else f"unavailable ({clock.err})"}
     result["wall_s_timed"] = wall
 
-    if not args.no_cpu and args.workload == "headline":
-        base, check = cpu_baseline(wl, q, k, v, o, max_heads=wl.B * wl.H)
-        result["cpu_baseline"] = base
-        result["parity_sample"] = check
-    if not args.no_cpu and is_bwd:
-        base, check = cpu_baseline_bwd(wl, q, k, v, dout, grads[:3], max_heads=wl.B * wl.H)
+    if not args.no_probe:
+        probe = run_probes(torch, fa, stream)
+        result["probe"] = probe
+        rf = result["roofline"]
+        if rf["bound"] == "mfma":
+            rf["frac_of_probe"] = rf["achieved"] / probe["mfma_bf16_tflops"]
+        elif rf["bound"] == "hbm":
+            rf["frac_of_probe"] = rf["achieved"] / probe["hbm_read_gbs"]
+
+    if not args.no_cpu and not is_decode:
+        torch.cuda.synchronize()
+        if is_bwd:
+            qs, ks, vs, ds = (si.torch_to_f64(x) for x in (q, k, v, dout))
+            gs = [si.torch_to_f64(g) for g in grads[:3]]
+            tasks = [("bwd", (b, h), (qs[b, h], ks[b, h], vs[b, h], ds[b, h]), wl.scale, wl.causal)
+                     for b in range(wl.B) for h in range(wl.H)]
+            per_head = 10.0 * wl.visible_pairs * wl.d
+
+            def compare(key, ref):
+                b, h = key
+                return [err_triplet(g[b, h], r[0, 0]) for g, r in zip(gs, ref)]
+
+            base, check = cpu_baseline(tasks, lambda key: per_head, args.cpu_budget_s, compare)
+            base["sample"] = (f"{check['tasks_checked']} of {len(tasks)} heads (dQ, dK, dV of all {wl.Nq} rows) of "
+                              f"the same inputs, fp64 numpy, one head per task")
+        else:
+            rows = 1024 if wl.Nq * wl.Nk >= 4096 * 4096 else wl.Nq
+            tasks = fwd_oracle_tasks(wl, q, k, v, rows)
+            og = si.torch_to_f64(o)
+
+            def pairs(key):
+                b, h, r0, r1 = key
+                if not wl.causal:
+                    return float(r1 - r0) * wl.Nk
+                off = wl.Nk - wl.Nq
+                return float(sum(min(wl.Nk, i + off + 1) for i in range(r0, r1)))
+
+            def compare(key, ref):
+                b, h, r0, r1 = key
+                return [err_triplet(og[b, h, r0:r1], ref)]
+
+            base, check = cpu_baseline(tasks, lambda key: 4.0 * wl.d * pairs(key), args.cpu_budget_s, compare)
+            base["sample"] = (f"{check['tasks_checked']} of {len(tasks)} tasks of {rows} query rows of one head "
+                              f"each, the same inputs, fp64 numpy")
         result["cpu_baseline"] = base
         result["parity_sample"] = check
     print(json.dumps(result), flush=True)

@@ -250,3 +250,27 @@ def merge_lse(part_lse, part_o, order=None, out_dtype=None, out=None, return_lse
                                        S, B, H, Nq, d, out.data_ptr(), _dtype_code(out_dtype),
                                        lse.data_ptr() if lse is not None else None, _stream_ptr(part_o.device)))
     return (out, lse) if return_lse else out
+
+
+def probe_mfma_bf16(nblocks=2048, iters=1024, out=None):
+    """Launch the matrix-core probe of fa_probe.h on the current stream; returns (flops, out).
+
+    ``out`` (optional) is a float32 device tensor of at least nblocks * 256 elements.
+    """
+    torch = _torch()
+    if out is None:
+        out = torch.empty(nblocks * 256, dtype=torch.float32, device="cuda")
+    _native.check(_native.fa_probe_mfma_bf16(out.data_ptr(), out.numel(), nblocks, iters, _stream_ptr(out.device)))
+    return float(nblocks) * 4 * iters * 8 * 32768, out
+
+
+def probe_hbm_read(buf, nblocks=4096, out=None):
+    """Launch the streaming-read probe of fa_probe.h over every byte of the device tensor ``buf``; returns the
+    number of bytes read. ``out`` (optional) is an int32 device tensor of at least nblocks * 256 elements."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(nblocks * 256, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _native.check(_native.fa_probe_hbm_read(buf.data_ptr(), nbytes, out.data_ptr(), out.numel(), nblocks,
+                                            _stream_ptr(buf.device)))
+    return nbytes

@@ -14,7 +14,8 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 256
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_fwd_lse", "fa_bwd", "fa_merge_states",
-           "fa_fwd_split_lse", "fa_merge_lse", "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_fwd_split_lse", "fa_merge_lse", "fa_status_string", "fa_last_error", "fa_abi_version",
+           "fa_probe_mfma_bf16", "fa_probe_hbm_read")
 
 _lib = None
 
@@ -51,6 +52,11 @@ def lib() -> ctypes.CDLL:
         L.fa_last_error.restype = ctypes.c_char_p
         L.fa_abi_version.argtypes = []
         L.fa_abi_version.restype = I
+        LL = ctypes.c_longlong
+        L.fa_probe_mfma_bf16.argtypes = [P, LL, I, I, P]
+        L.fa_probe_mfma_bf16.restype = I
+        L.fa_probe_hbm_read.argtypes = [P, LL, P, LL, I, P]
+        L.fa_probe_hbm_read.restype = I
         _lib = L
     return _lib
 
@@ -122,3 +128,11 @@ def fa_last_error() -> str:
 
 def fa_abi_version() -> int:
     return lib().fa_abi_version()
+
+
+def fa_probe_mfma_bf16(out, out_elems, nblocks, iters, stream):
+    return lib().fa_probe_mfma_bf16(out, out_elems, nblocks, iters, stream)
+
+
+def fa_probe_hbm_read(src, nbytes, out, out_elems, nblocks, stream):
+    return lib().fa_probe_hbm_read(src, nbytes, out, out_elems, nblocks, stream)

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libfa.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["fa_api.hip", "fwd_mfma.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd.hip"]
+SOURCES = ["fa_api.hip", "fwd_mfma.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd.hip", "probe.hip"]
 # Packed fp32 VALU instructions are disabled for every device pass.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "fa_probe.h"
 #include "fa_internal.h"
 
 namespace {
@@ -31,6 +32,19 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return na && nb && x < y + nb && y < x + na;
+}
+
+// True when some output buffer overlaps an input buffer or another output (null or empty buffers
+// overlap nothing).
+bool outputs_overlap(const void* const* outs, const size_t* outsz, int nout, const void* const* ins,
+                     const size_t* insz, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return true;
+  }
+  return false;
 }
 
 // Shape, dtype and scale checks shared by fa_fwd and fa_fwd_split.
@@ -116,8 +130,13 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
   const size_t obytes = (size_t)B * H * Nq * d * dtype_size(out_dtype);
   const size_t qbytes = (size_t)B * H * Nq * d * dtype_size(in_dtype);
   const size_t kvbytes = (size_t)B * H_kv * Nk * d * dtype_size(in_dtype);
-  if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, kvbytes) || overlaps(o, obytes, v, kvbytes))
-    return fail(FA_EINVAL, "%s: o overlaps q, k or v", fn);
+  const size_t rbytes = (size_t)B * H * Nq * sizeof(float);
+  const void* ins[] = {q, k, v};
+  const size_t insz[] = {qbytes, kvbytes, kvbytes};
+  const void* outs[] = {o, m_out, l_out, lse_out};
+  const size_t outsz[] = {obytes, m_out ? rbytes : 0, l_out ? rbytes : 0, lse_out ? rbytes : 0};
+  if (outputs_overlap(outs, outsz, 4, ins, insz, 3))
+    return fail(FA_EINVAL, "%s: an output (o, m_out, l_out, lse) overlaps q, k, v or another output", fn);
 
   fa::FwdArgs a = make_args(q, k, v, B, H, H_kv, Nq, Nk, scale, causal);
   a.o = o;
@@ -147,6 +166,16 @@ fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const voi
   if (!aligned16(part_o) || !aligned4(part_m) || !aligned4(part_l))
     return fail(FA_EINVAL, "%s: part_o must be 16-byte and part_m, part_l 4-byte aligned", fn);
   if ((size_t)B * H == 0 || Nq == 0) return FA_OK;
+  {
+    const size_t es = dtype_size(in_dtype), rows = (size_t)num_splits * B * H * Nq;
+    const size_t qbytes = (size_t)B * H * Nq * d * es, kvbytes = (size_t)B * H_kv * Nk * d * es;
+    const void* ins[] = {q, k, v};
+    const size_t insz[] = {qbytes, kvbytes, kvbytes};
+    const void* outs[] = {part_m, lse_form ? nullptr : part_l, part_o};
+    const size_t outsz[] = {rows * 4, lse_form ? 0 : rows * 4, rows * d * 4};
+    if (outputs_overlap(outs, outsz, 3, ins, insz, 3))
+      return fail(FA_EINVAL, "%s: a partial-state buffer overlaps q, k, v or another partial-state buffer", fn);
+  }
 
   fa::FwdArgs a = make_args(q, k, v, B, H, H_kv, Nq, Nk, scale, causal);
   a.part_m = part_m;
@@ -192,6 +221,16 @@ fa_status merge_impl(const char* fn, bool lse_form, const float* part_m, const f
   const long long rows = (long long)B * H * Nq;
   if (rows == 0) return FA_OK;
   if (rows > 0x7fffffffLL) return fail(FA_EINVAL, "%s: B*H*Nq=%lld exceeds 2^31-1", fn, rows);
+  {
+    const size_t r = (size_t)rows, st = (size_t)num_splits * r;
+    const void* ins[] = {part_m, lse_form ? nullptr : part_l, part_o};
+    const size_t insz[] = {st * 4, lse_form ? 0 : st * 4, st * d * 4};
+    const void* outs[] = {o, m_out, l_out, lse_out};
+    const size_t outsz[] = {r * d * dtype_size(out_dtype), m_out ? r * 4 : 0, l_out ? r * 4 : 0,
+                            lse_out ? r * 4 : 0};
+    if (outputs_overlap(outs, outsz, 4, ins, insz, 3))
+      return fail(FA_EINVAL, "%s: an output (o, m_out, l_out, lse) overlaps a partial state or another output", fn);
+  }
   a.part_m = part_m;
   a.part_l = part_l;
   a.part_o = part_o;
@@ -328,6 +367,31 @@ fa_status fa_merge_lse(const float* part_lse, const float* part_o, const int* or
   g_last_error[0] = 0;
   return merge_impl("fa_merge_lse", true, part_lse, nullptr, part_o, order, num_splits, B, H, Nq, d, o, out_dtype,
                     nullptr, nullptr, lse_out, stream);
+}
+
+fa_status fa_probe_mfma_bf16(float* out, long long out_elems, int nblocks, int iters, void* stream) {
+  g_last_error[0] = 0;
+  const char* fn = "fa_probe_mfma_bf16";
+  if (nblocks < 1 || nblocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return fail(FA_EINVAL, "%s: nblocks=%d and iters=%d must be in [1, 2^20]", fn, nblocks, iters);
+  if (!out || !aligned4(out) || out_elems < (long long)nblocks * 256)
+    return fail(FA_EINVAL, "%s: out must be a 4-byte aligned device buffer of >= nblocks * 256 = %lld floats", fn,
+                (long long)nblocks * 256);
+  return launched(fn, fa::launch_probe_mfma(out, nblocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_probe_hbm_read(const void* src, long long bytes, unsigned* out, long long out_elems, int nblocks,
+                            void* stream) {
+  g_last_error[0] = 0;
+  const char* fn = "fa_probe_hbm_read";
+  if (nblocks < 1 || nblocks > (1 << 20)) return fail(FA_EINVAL, "%s: nblocks=%d must be in [1, 2^20]", fn, nblocks);
+  if (!src || !aligned16(src) || bytes <= 0 || bytes % 16 != 0)
+    return fail(FA_EINVAL, "%s: src must be 16-byte aligned and bytes=%lld a positive multiple of 16", fn, bytes);
+  if (!out || !aligned4(out) || out_elems < (long long)nblocks * 256)
+    return fail(FA_EINVAL, "%s: out must be a 4-byte aligned device buffer of >= nblocks * 256 = %lld values", fn,
+                (long long)nblocks * 256);
+  if (overlaps(src, (size_t)bytes, out, (size_t)out_elems * 4)) return fail(FA_EINVAL, "%s: out overlaps src", fn);
+  return launched(fn, fa::launch_probe_read(src, (size_t)bytes, out, nblocks, static_cast<hipStream_t>(stream)));
 }
 
 const char* fa_status_string(int status) {

@@ -365,7 +365,11 @@ __device__ __forceinline__ void mfma_phase_order_d128() {
 // rate). Reads, waits and MFMAs are inline asm so that the order is kept. Each wait takes the
 // registers it guards as in-out operands, so no MFMA that reads them can be placed before it.
 // The compiler does not see the MFMA latency inside asm, so the sequence ends with the wait
-// states a VALU read of an MFMA result needs.
+// states a VALU read of an MFMA result needs, in an asm statement that takes every S and PV
+// accumulator as an in-out operand: no instruction that reads or writes them can be placed
+// between the last MFMA and the end of those wait states. (Written with compiler-visible
+// MFMAs and LDS loads instead, the compiler must assume the loads may alias the direct-to-LDS
+// tile loads in flight and waits for those before the first read: 2.4 % slower.)
 #define FA_RD(dst, addr, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(dst) : "v"(addr))
 #define FA_WAIT0(x, y) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y))
 #define FA_MF_BF16(acc, a, b) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
@@ -425,8 +429,12 @@ __device__ __forceinline__ void mfma_phase_d64(unsigned vaddr, const unsigned (&
   mfma_acc<T>(s[0][0], r1a, qf[0][3]);
   mfma_acc<T>(s[1][0], r1a, qf[1][3]); mfma_acc<T>(s[0][1], r1b, qf[0][3]);
   mfma_acc<T>(s[1][1], r1b, qf[1][3]);
-  // an MFMA result read by the VALU needs 18 wait states after the MFMA (16-pass worst case)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  // On gfx950 a VALU or memory access of a 16-pass MFMA's result needs passes + 4 = 20 wait
+  // states after the MFMA; these are 20 (s_nop N waits N + 1). The accumulators are operands, so
+  // every access of them follows (tests/test_mfma_asm_hazards.py checks the built code).
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]), "+v"(acc[0][0]), "+v"(acc[0][1]),
+                 "+v"(acc[1][0]), "+v"(acc[1][1])::"memory");
 }
 
 template <int D, typename T, bool FAST, bool CAUSAL>

@@ -5,7 +5,7 @@
 // (derived from the recurrence of "从零手写 FlashAttention" §4):
 //   m = max(m_a, m_b);  l = l_a e^(m_a - m) + l_b e^(m_b - m);  o = o_a e^(m_a - m) + o_b e^(m_b - m)
 // A state with m = -inf holds no keys and gets weight 0, so -inf - (-inf) is never evaluated.
-// The answer is o / l. One thread handles 4 columns of one row; the partial-state reads are
+// The answer is o / l; a row whose states are all empty (l = 0) gets O = 0, as in the (lse, o) form. One thread handles 4 columns of one row; the partial-state reads are
 // coalesced 16-byte loads.
 
 #include "fa_internal.h"
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int i = 0; i < 4; ++i) o[i] = o[i] * wa + os[i] * wb;
     m = mn;
   }
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   const size_t e = (size_t)row * D + c;
   if (a.out_dtype == kF32) {
     f32x4_t x = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};

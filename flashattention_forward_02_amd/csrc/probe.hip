@@ -1,0 +1,82 @@
+// Measurement probes: the empirical ceilings the attention kernels are compared against.
+//
+//  * probe_mfma_kernel: back-to-back 32x32x16 bf16 MFMAs on register operands, eight independent
+//    accumulators per wave so the matrix core never waits on a result. Its rate is the
+//    matrix-core throughput this chip sustains at the clock it runs at under that load.
+//  * probe_read_kernel: a streaming 16-byte-per-lane read of a large buffer (each byte once), the
+//    HBM read bandwidth a memory-bound kernel can reach.
+//
+// Neither touches memory outside the buffers the host checked; both write one value per thread
+// so the work cannot be removed.
+
+#include "fa_internal.h"
+#include "mfma_common.h"
+
+namespace fa {
+namespace {
+
+constexpr int kProbeThreads = 256;   // 4 waves
+constexpr int kProbeChains = 8;      // independent accumulators per wave
+
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  // small operands (|x| <= 2^-8): the accumulators stay finite for any iteration count used here
+  const float av = (float)(lane & 7) * (1.f / 2048.f), bv = (float)((lane >> 3) & 7) * (1.f / 2048.f);
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(av + (float)i * (1.f / 4096.f));
+    b[i] = (__bf16)(bv - (float)i * (1.f / 4096.f));
+  }
+  f32x16_t acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ src, size_t n16,
+                                                                    unsigned* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * kProbeThreads;
+  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  unsigned x = 0u;
+  // four independent loads in flight per lane; the tail loop takes what is left
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t v0 = __builtin_nontemporal_load(&src[i]);
+    const u32x4_t v1 = __builtin_nontemporal_load(&src[i + stride]);
+    const u32x4_t v2 = __builtin_nontemporal_load(&src[i + 2 * stride]);
+    const u32x4_t v3 = __builtin_nontemporal_load(&src[i + 3 * stride]);
+    x ^= (v0[0] ^ v0[1] ^ v0[2] ^ v0[3]) ^ (v1[0] ^ v1[1] ^ v1[2] ^ v1[3]) ^ (v2[0] ^ v2[1] ^ v2[2] ^ v2[3]) ^
+         (v3[0] ^ v3[1] ^ v3[2] ^ v3[3]);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = __builtin_nontemporal_load(&src[i]);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = x;
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma(float* out, int nblocks, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)nblocks), dim3(kProbeThreads), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, size_t bytes, unsigned* out, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)nblocks), dim3(kProbeThreads), 0, s,
+                     static_cast<const u32x4_t*>(src), bytes / 16, out);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -64,7 +64,7 @@ typedef enum { FA_OK = 0, FA_EINVAL = 1, FA_EUNSUPPORTED = 2, FA_EHIP = 3 } fa_s
  *   o         [B,H,Nq,d] in `out_dtype`, which is FA_F32 or equal to `in_dtype`.
  *   m_out, l_out  optional [B,H,Nq] fp32 row statistics (see above), or NULL.
  *   scale     finite and >= 0; usually 1/sqrt(d) (the pages' scale). 0 gives uniform weights.
- * o must not overlap q, k or v.
+ * No output (o, m_out, l_out) may overlap an input or another output (FA_EINVAL).
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
                  float* m_out, float* l_out,
@@ -81,7 +81,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
  *   part_l [S,B,H,Nq] fp32   l = sum over the part's keys of exp(S_ij - m)
  *   part_o [S,B,H,Nq,d] fp32 o = sum over the part's keys of exp(S_ij - m) * V_j  (NOT divided by l)
  * with S = num_splits, 1 <= num_splits <= min(Nk, FA_MAX_SPLITS). fa_merge_states combines
- * them; the merged result equals fa_fwd's up to rounding. The caller owns the three buffers.
+ * them; the merged result equals fa_fwd's up to rounding. The caller owns the three buffers,
+ * which must not overlap q, k, v or one another (FA_EINVAL).
  */
 fa_status fa_fwd_split(const void* q, const void* k, const void* v,
                        float* part_m, float* part_l, float* part_o,
@@ -121,7 +122,7 @@ fa_status fa_fwd_ext(const void* q, const void* k, const void* v, void* o,
  * 01_online_softmax.py" notes that FlashAttention-2 keeps a single number per row instead, the
  * log-sum-exp L = m + ln(l), from which P_ij = exp(S_ij - L_i).
  *   lse  [B,H,Nq] fp32, receives L_i = m_i + ln(l_i) of the scaled scores S (natural log).
- * Everything else as in fa_fwd_ext (this call computes the running maximum exactly).
+ * Everything else as in fa_fwd_ext. lse must not overlap q, k, v or o.
  */
 fa_status fa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
@@ -177,8 +178,11 @@ fa_status fa_fwd_split_ext(const void* q, const void* k, const void* v,
  * the rule that makes the result independent of the order up to rounding ("CS349E 第 11 讲
  * 01_online_softmax.py" demo 2, derived from the recurrence of "从零手写 FlashAttention" §4).
  * A part with m = -inf (no keys) has weight 0. Finally O = o / l in `out_dtype` (FA_F32,
- * FA_BF16 or FA_F16), and, when not NULL, m_out / l_out receive the merged m and l.
- * Layouts as in fa_fwd_split; o is [B,H,Nq,d].
+ * FA_BF16 or FA_F16), and, when not NULL, m_out / l_out receive the merged m and l. A row whose
+ * parts are all empty (possible under the causal mask of fa_fwd_split_ext only for rows that see
+ * no key at all) gets O = 0, m = -inf, l = 0.
+ * Layouts as in fa_fwd_split; o is [B,H,Nq,d]. No output (o, m_out, l_out) may overlap a partial
+ * state or another output (FA_EINVAL).
  */
 fa_status fa_merge_states(const float* part_m, const float* part_l, const float* part_o,
                           const int* order, int num_splits, int B, int H, int Nq, int d,

@@ -188,55 +188,62 @@ def online_softmax(x) -> np.ndarray:
 # The one-pass (m, l, acc) recurrence
 # ---------------------------------------------------------------------------
 
-def online_attention_row(q, K, V, block: int, scale=None, trace=None) -> np.ndarray:
-    """One query against all keys in a single pass, ``block`` keys at a time.
+def _key_blocks(n: int, block: int):
+    """Key ranges [start, stop) of consecutive blocks of ``block`` keys (the last one may be shorter)."""
+    return [(b0, min(n, b0 + block)) for b0 in range(0, n, block)]
 
-    [CS349E-L11] ``attn_row_1pass`` / demo 1; [FA-Simplified §2.3]: the state is
-    the running maximum m (starts at -inf), the running sum l (0) and the
-    accumulator acc (0, length dv). For each block of scores s:
-    m' = max(m, max s); alpha = exp(m - m') (0 on the first block);
-    l = alpha*l + sum exp(s - m'); acc = alpha*acc + exp(s - m') V_block; m = m'.
-    The answer is acc / l. Ragged last blocks are taken as they come. When
-    ``trace`` is a list, (block index, block max, m', alpha, l) is appended per
-    block (the table the demo prints).
+
+def online_attention_row(q, K, V, block: int, scale=None, history=None) -> np.ndarray:
+    """One query against all keys in a single pass over blocks of ``block`` keys.
+
+    [FA-Simplified §2.3] (the recurrence of [CS349E-L11] demo 1): the row's state starts
+    as the empty state (m, l, acc) = (-inf, 0, 0), and each block is folded into it. A
+    block contributes its own partial state (its maximum, its sum of exponentials, its
+    weighted sum of V rows), and folding it in is the merge rule of ``merge_states``:
+    the side whose maximum is lower is scaled by exp(m_side - m_new), which is exactly
+    the correction factor exp(m_old - m_new) the page applies to l and acc when a block
+    raises the maximum (and 0 for the empty start state). The answer is acc / l.
+    When ``history`` is a list, the running (m, l) after each block is appended.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[0])
-    m, l = NEG_INF, 0.0
-    acc = np.zeros(V.shape[1])
-    for b, start in enumerate(range(0, K.shape[0], block)):
-        s = float(scale) * (K[start:start + block] @ q)
-        m_next = max(m, float(s.max()))
-        alpha = math.exp(m - m_next)
-        p = np.exp(s - m_next)
-        l = alpha * l + float(p.sum())
-        acc = alpha * acc + p @ V[start:start + block]
-        if trace is not None:
-            trace.append((b, float(s.max()), m_next, alpha, l))
-        m = m_next
-    return acc / l
+    state = (np.array([NEG_INF]), np.zeros(1), np.zeros((1, V.shape[1])))
+    for b0, b1 in _key_blocks(K.shape[0], block):
+        s_block = float(scale) * (K[b0:b1] @ q)
+        state = merge_states(state, partial_state(s_block[None, :], V[b0:b1]))
+        if history is not None:
+            history.append((float(state[0][0]), float(state[1][0])))
+    return finish_state(state)[0]
 
 
 def two_pass_attention_row(q, K, V, block: int, scale=None) -> np.ndarray:
-    """[CS349E-L11] ``attn_row_2pass``: one scan for (m, l), a second scan recomputing the scores for sum p V / l."""
+    """Two scans over key blocks ([CS349E-L11] demo 1's two-pass variant): statistics, then weights.
+
+    Scan one reduces the blocks' scores to the row's (m, l) without storing them across
+    blocks: every block gives (max, sum exp(s - max)), and the row's statistics are
+    m = max over blocks, l = sum over blocks of l_b exp(m_b - m). Scan two recomputes each
+    block's scores and adds exp(s - m) / l times that block's V rows.
+    """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[0])
-    m, l = NEG_INF, 0.0
-    for start in range(0, K.shape[0], block):
-        s = float(scale) * (K[start:start + block] @ q)
-        m_next = max(m, float(s.max()))
-        l = l * math.exp(m - m_next) + float(np.exp(s - m_next).sum())
-        m = m_next
+    blocks = _key_blocks(K.shape[0], block)
+    stats = np.empty((len(blocks), 2))
+    for i, (b0, b1) in enumerate(blocks):
+        s_block = float(scale) * (K[b0:b1] @ q)
+        stats[i, 0] = s_block.max()
+        stats[i, 1] = np.exp(s_block - stats[i, 0]).sum()
+    m = stats[:, 0].max()
+    l = float(np.sum(stats[:, 1] * np.exp(stats[:, 0] - m)))
     out = np.zeros(V.shape[1])
-    for start in range(0, K.shape[0], block):
-        s = float(scale) * (K[start:start + block] @ q)
-        out += (np.exp(s - m) / l) @ V[start:start + block]
+    for b0, b1 in blocks:
+        w = np.exp(float(scale) * (K[b0:b1] @ q) - m) / l
+        out += w @ V[b0:b1]
     return out
 
 
@@ -285,32 +292,31 @@ def online_attention(q, k, v, scale, Br: int, Bc: int, return_stats: bool = Fals
 
 
 def fa1_order_attention(q, k, v, scale, block: int) -> np.ndarray:
-    """The K/V-outer, Q-inner order that renormalises O at every step ([FA-Fill Exercise 4]).
+    """K/V blocks in the outer loop, with O kept normalised after every block ([FA-Fill Exercise 4]).
 
-    For each K/V block j, for each Q block i: S = scale Q_i K_j^T; m' = max(m_i, rowmax S);
-    P = exp(S - m'); l' = l_i exp(m_i - m') + rowsum P;
-    O_i = O_i (l_i exp(m_i - m') / l') + (P V_j) / l'; then l_i = l', m_i = m'.
-    O is normalised at every step, so nothing is divided at the end. Single head [N, d].
+    The query blocks of the exercise's inner loop are independent of one another, so all
+    query rows are updated together here. Per K/V block j, for every row: the new maximum
+    m' = max(m, rowmax S_j); the mass carried over from earlier blocks, l exp(m - m'); the new
+    total l' = carried + rowsum exp(S_j - m'); and O, which always holds the normalised
+    output of the keys seen so far, becomes the l'-weighted mix of the old O (weight
+    carried / l') and of this block's exp(S_j - m') V_j / l'. Nothing is divided at the end.
+    Single head: q [Nq, d], k, v [Nk, d].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    Nq, Nk = q.shape[0], k.shape[0]
+    Nq = q.shape[0]
     O = np.zeros((Nq, v.shape[1]))
     l = np.zeros(Nq)
     m = np.full(Nq, NEG_INF)
-    for j0 in range(0, Nk, block):
-        Kj, Vj = k[j0:j0 + block], v[j0:j0 + block]
-        for i0 in range(0, Nq, block):
-            rows = slice(i0, i0 + block)
-            S = float(scale) * (q[rows] @ Kj.T)
-            m_next = np.maximum(m[rows], S.max(axis=1))
-            P = np.exp(S - m_next[:, None])
-            carried = l[rows] * np.exp(m[rows] - m_next)
-            l_next = carried + P.sum(axis=1)
-            O[rows] = O[rows] * (carried / l_next)[:, None] + (P @ Vj) / l_next[:, None]
-            l[rows] = l_next
-            m[rows] = m_next
+    for b0, b1 in _key_blocks(k.shape[0], block):
+        S = float(scale) * (q @ k[b0:b1].T)
+        m_new = np.maximum(m, S.max(axis=1))
+        E = np.exp(S - m_new[:, None])
+        carried = l * np.exp(m - m_new)
+        total = carried + E.sum(axis=1)
+        O = (carried / total)[:, None] * O + (E @ v[b0:b1]) / total[:, None]
+        m, l = m_new, total
     return O
 
 
@@ -381,9 +387,18 @@ def merge_tree(states):
 
 
 def finish_state(state):
-    """o / l: the attention output of a (merged) state ([CS349E-L11] demo 2)."""
+    """o / l: the attention output of a (merged) state ([CS349E-L11] demo 2).
+
+    A row whose state is empty (l = 0: none of its parts held a key the row may see) has no
+    softmax to finish; it gets O = 0, the value the (lse, o) form gives such a row.
+    """
     m, l, o = state
-    return o / l[..., None]
+    l = np.asarray(l, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    out = np.zeros_like(o)
+    live = l > 0
+    out[live] = o[live] / l[live][..., None]
+    return out
 
 
 def split_bounds(Nk: int, num_splits: int):

@@ -187,6 +187,8 @@ BWD_BF16 = Workload("backward B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 
 # The backward pass on the causal workload (same draws, the causal mask).
 BWD_CAUSAL_BF16 = Workload("backward causal B=4 H=16 N=4096 d=64 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 64, "bf16",
                            3, causal=True)
+# The backward pass at d = 128 on the headline batch shape (per-head draws of seed 3 at d = 128).
+BWD_D128_BF16 = Workload("backward B=4 H=16 N=4096 d=128 bf16 (dO: tensor 3)", 4, 16, 4096, 4096, 128, "bf16", 3)
 GQA_DECODE_BF16 = Workload("gqa_decode B=16 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 6,
                            num_splits=16, H_kv=8)
 DECODE_BF16 = Workload("split_kv_decode B=16 H=32 Nq=1 Nk=32768 d=128 bf16", 16, 32, 1, 32768, 128, "bf16", 5,

@@ -10,16 +10,19 @@ import flashattention_forward_02_amd as fa
 from flashattention_forward_02_amd import _native as n
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 # Fake, 16-byte aligned, never dereferenced: every call below fails validation first.
 P = 0x10000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_exports():
@@ -286,4 +289,55 @@ def merge_lse(**kw):
 ])
 def test_fa_merge_lse_rejects(kw, status, msg):
     assert merge_lse(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(m_out=P), dict(l_out=P + 16), dict(m_out=P * 2), dict(m_out=P * 8, l_out=P * 8)])
+def test_fa_fwd_rejects_overlapping_outputs(kw):
+    """m_out / l_out may overlap neither an input, o, nor each other."""
+    assert fwd(**kw) == n.FA_EINVAL
+    assert "overlaps" in n.fa_last_error()
+
+
+def test_fa_fwd_lse_rejects_lse_overlapping_o():
+    assert fwd_lse(lse=P * 2) == n.FA_EINVAL
+    assert "overlaps" in n.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(part_m=P), dict(part_l=P * 2), dict(part_o=P * 2)])
+def test_fa_fwd_split_rejects_overlapping_states(kw):
+    assert split(**kw) == n.FA_EINVAL
+    assert "overlaps" in n.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(o=P * 3), dict(o=P), dict(m_out=P * 5, l_out=P * 5), dict(m_out=P * 2)])
+def test_fa_merge_states_rejects_overlapping_outputs(kw):
+    assert merge(**kw) == n.FA_EINVAL
+    assert "overlaps" in n.fa_last_error()
+
+
+def test_fa_merge_lse_rejects_output_overlapping_states():
+    assert merge_lse(o=P * 2) == n.FA_EINVAL
+    assert "overlaps" in n.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(nblocks=0), "nblocks"), (dict(iters=0), "iters"), (dict(nblocks=(1 << 20) + 1), "nblocks"),
+    (dict(out=None), "out"), (dict(out_elems=255), "out"), (dict(out=P + 2), "out"),
+])
+def test_probe_mfma_rejects(kw, msg):
+    a = dict(out=P, out_elems=256, nblocks=1, iters=4, stream=None)
+    a.update(kw)
+    assert n.fa_probe_mfma_bf16(**a) == n.FA_EINVAL
+    assert msg in n.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(src=P + 4), "aligned"), (dict(nbytes=100), "multiple of 16"), (dict(nbytes=0), "multiple of 16"),
+    (dict(out_elems=10), "out"), (dict(out=P + 64), "overlaps"), (dict(nblocks=0), "nblocks"),
+])
+def test_probe_hbm_read_rejects(kw, msg):
+    a = dict(src=P, nbytes=1 << 20, out=P * 1000, out_elems=256, nblocks=1, stream=None)
+    a.update(kw)
+    assert n.fa_probe_hbm_read(**a) == n.FA_EINVAL
     assert msg in n.fa_last_error()

@@ -157,13 +157,19 @@ def test_one_pass_equals_three_pass_demo1():
     two = oracle.two_pass_attention_row(q, K, V, 256)
     assert np.max(np.abs(one - ref)) < 1e-15
     assert np.max(np.abs(two - ref)) < 1e-15
-    trace = []
-    oracle.online_attention_row(q, K[:1024], V[:1024], 256, trace=trace)
-    assert [t[0] for t in trace] == [0, 1, 2, 3]
-    assert trace[0][3] == 0.0                                # alpha = exp(-inf) = 0 on the first block
-    ms = [t[2] for t in trace]
-    assert all(b >= a for a, b in zip(ms, ms[1:]))          # the running max never decreases
-    assert all(0.0 <= t[3] <= 1.0 for t in trace)
+    # the running state block by block: the maximum never decreases; after the first block the
+    # empty start state has weight 0, so (m, l) are that block's own maximum and sum
+    hist = []
+    oracle.online_attention_row(q, K[:1024], V[:1024], 256, history=hist)
+    assert len(hist) == 4
+    s0 = (K[:256] @ q) / 8.0
+    assert hist[0][0] == s0.max()
+    assert abs(hist[0][1] - np.exp(s0 - s0.max()).sum()) < 1e-12
+    ms = [h[0] for h in hist]
+    assert all(b >= a for a, b in zip(ms, ms[1:]))
+    s_all = (K[:1024] @ q) / 8.0
+    assert ms[-1] == s_all.max()
+    assert abs(hist[-1][1] - np.exp(s_all - s_all.max()).sum()) < 1e-12
 
 
 @pytest.mark.parametrize("Br,Bc", [(64, 64), (1, 256), (48, 80), (256, 7)])
@@ -224,6 +230,11 @@ def test_merge_empty_states_are_identity():
             assert np.array_equal(x, y)
     both = oracle.merge_states(empty, empty)
     assert np.all(both[0] == -np.inf) and np.all(both[1] == 0) and not np.any(np.isnan(both[2]))
+    # a row with no key at all finishes as O = 0 (the value the (lse, o) form gives it), not 0 / 0;
+    # the other rows finish as o / l
+    mixed = (np.array([both[0][0], a[0][1]]), np.array([0.0, a[1][1]]), np.stack([both[2][0], a[2][1]]))
+    fin = oracle.finish_state(mixed)
+    assert np.all(fin[0] == 0.0) and np.allclose(fin[1], a[2][1] / a[1][1], rtol=1e-15, atol=0)
 
 
 @pytest.mark.parametrize("Nk,S", [(100, 7), (64, 64), (5000, 16), (33, 1)])

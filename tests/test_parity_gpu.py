@@ -33,10 +33,14 @@ def say(msg):
 
 
 def run_case(q, k, v, dtype, scale, out_dtype="f32", stats=True):
-    """Run fa_fwd on host Tensors; return O, m, l as float64 numpy plus the device tensors."""
+    """Run fa_fwd on host Tensors; return O, m, l as float64 numpy (m, l are None when ``stats`` is False:
+    the call then asks for O only, which the matrix-core kernel serves with its sum-checked softmax)."""
     qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
-    o, m, l = fa.fwd(qd, kd, vd, scale=scale, out_dtype=_tdt(out_dtype), return_stats=True)
+    res = fa.fwd(qd, kd, vd, scale=scale, out_dtype=_tdt(out_dtype), return_stats=stats)
     torch.cuda.synchronize()
+    if not stats:
+        return si.torch_to_f64(res), None, None
+    o, m, l = res
     return si.torch_to_f64(o), si.torch_to_f64(m), si.torch_to_f64(l)
 
 
@@ -326,6 +330,28 @@ def test_split_states_and_merge_orders(dtype, shape):
         assert np.max(np.abs(o - outs[0])) < 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_of_all_empty_parts_gives_zero(d):
+    """A row whose parts hold no key (every part m = -inf, l = 0, o = 0) merges to O = 0, m = -inf, l = 0
+    (no 0 / 0); the other rows of the same call are o / l of their parts."""
+    S, rows = 3, 5
+    r = np.random.default_rng(d)
+    pm = r.standard_normal((S, 1, 1, rows)).astype(np.float32)
+    pl = (1.0 + r.random((S, 1, 1, rows))).astype(np.float32)
+    po = r.standard_normal((S, 1, 1, rows, d)).astype(np.float32)
+    pm[:, 0, 0, 2] = -np.inf
+    pl[:, 0, 0, 2] = 0.0
+    po[:, 0, 0, 2] = 0.0
+    o, m, l = fa.merge_states(*[torch.from_numpy(x).to(DEV) for x in (pm, pl, po)], return_stats=True)
+    torch.cuda.synchronize()
+    o, m, l = si.torch_to_f64(o), si.torch_to_f64(m), si.torch_to_f64(l)
+    assert np.all(o[0, 0, 2] == 0.0) and m[0, 0, 2] == -np.inf and l[0, 0, 2] == 0.0
+    states = [(pm[c, 0, 0].astype(np.float64), pl[c, 0, 0].astype(np.float64), po[c, 0, 0].astype(np.float64))
+              for c in range(S)]
+    ref = oracle.finish_state(oracle.merge_sequential(states))
+    assert np.max(np.abs(o[0, 0] - ref)) < 1e-5
+
+
 def test_decode_bf16_full_size_split16_shuffled_merge():
     """B=16, H=32, one query, Nk=32768, d=128 bf16; 16 splits merged in default_rng(5).permutation(16) order."""
     w = si.DECODE_BF16
@@ -416,19 +442,21 @@ def test_no_stats_path(dtype, shape):
     assert_close(o, ref, dtype, f"no-stats {dtype} {shape}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("kmul,shift", [(1.0, 0.0), (3.0, 0.0), (1.0, 100.0), (8.0, 0.0)])
-def test_no_stats_path_score_ranges(kmul, shift):
+def test_no_stats_path_score_ranges(kmul, shift, d):
     """Keys x3 and x8 (wide score ranges, so the reference moves on later tiles) and scores shifted
-    to about 100 (exponents far from 0 in every tile)."""
-    q, k, v = si.small_case(77, 1, 2, 300, 2000, 64, "bf16", k_mult=kmul)
+    to about 100 (exponents far from 0 in every tile), at both head dims."""
+    q, k, v = si.small_case(77 + d, 1, 2, 300, 2000, d, "bf16", k_mult=kmul)
     qf = q.as_f64()
+    sc = si.fp32_inverse_sqrt(d)
     if shift:
         u = qf[0, 0].mean(axis=0)
-        u = u * (shift / (0.125 * float(u @ u)))
+        u = u * (shift / (sc * float(u @ u)))
         k = si.encode((k.as_f64() + u).astype(np.float32), "bf16")
-    o = run_nostats(q, k, v, 0.125)
-    ref = oracle.attention_fp64(qf, k.as_f64(), v.as_f64(), 0.125)
-    assert_close(o, ref, "bf16", f"no-stats kmul={kmul} shift={shift}")
+    o = run_nostats(q, k, v, sc)
+    ref = oracle.attention_fp64(qf, k.as_f64(), v.as_f64(), sc)
+    assert_close(o, ref, "bf16", f"no-stats d={d} kmul={kmul} shift={shift}")
 
 
 def test_no_stats_increasing_scores_across_tiles():
@@ -451,19 +479,42 @@ def test_no_stats_zero_scale():
 
 
 def test_headline_bf16_full_size_no_stats():
-    """The benchmarked launch exactly (no statistics requested), sampled rows from 8 heads."""
+    """The benchmarked launch exactly (no statistics requested): 6 whole heads (all 4096 rows), one from
+    each batch entry and both ends of the head range, plus sampled rows from 8 more heads."""
     w = si.HEADLINE_BF16
     q, k, v = si.workload_inputs(w)
-    o = run_nostats(q, k, v, w.scale)
+    o, _, _ = run_case(q, k, v, "bf16", w.scale, stats=False)
     qf, kf, vf = q.as_f64(), k.as_f64(), v.as_f64()
     rng = np.random.default_rng(33)
     got, ref = [], []
+    for (b, h) in [(0, 0), (1, 15), (2, 7), (3, 8), (3, 15), (0, 10)]:
+        got.append(o[b, h])
+        ref.append(oracle.attention_rows_fp64(qf[b, h], kf[b, h], vf[b, h], w.scale)[0])
     for (b, h) in [(0, 1), (1, 7), (2, 14), (3, 3), (0, 9), (1, 0), (2, 5), (3, 12)]:
         rows = np.sort(rng.choice(w.Nq, size=256, replace=False))
         got.append(o[b, h, rows])
         ref.append(oracle.attention_rows_fp64(qf[b, h, rows], kf[b, h], vf[b, h], w.scale)[0])
     say(f"headline no-stats errors {errors(np.concatenate(got), np.concatenate(ref))}")
     assert_close(np.concatenate(got), np.concatenate(ref), "bf16", "headline no-stats")
+    assert np.all(np.isfinite(o))
+
+
+def test_long_seq_bf16_full_size_no_stats_whole_heads():
+    """B=1, H=32, N=16384, d=128 bf16, K x3, O only (the benchmarked launch, sum-checked softmax): two whole
+    heads (all 16384 rows each) against the oracle, and every output finite."""
+    w = si.LONG_SEQ_BF16
+    say("long_seq no-stats: generating inputs")
+    q, k, v = si.workload_inputs(w)
+    say("long_seq no-stats: running fa_fwd")
+    o, _, _ = run_case(q, k, v, "bf16", w.scale, stats=False)
+    assert np.all(np.isfinite(o))
+    got, ref = [], []
+    for h in (5, 30):
+        qh, kh, vh = (si.bf16_bits_to_f32(x.data[0, h]).astype(np.float64) for x in (q, k, v))
+        ref.append(oracle.attention_fp64(qh[None], kh[None], vh[None], w.scale)[0])
+        got.append(o[0, h])
+        say(f"long_seq no-stats: head {h} errors {errors(got[-1], ref[-1])}")
+    assert_close(np.concatenate(got), np.concatenate(ref), "bf16", "long seq no-stats whole heads")
 
 
 @pytest.mark.parametrize("causal", [False, True])

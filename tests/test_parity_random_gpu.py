@@ -5,6 +5,7 @@ Each case draws (B, H, H_kv, Nq, Nk, d, causal, dtype) from its own seeded gener
 names a case that reruns alone. Sizes stay small enough for the oracle to finish in well under a
 second; the fixed-shape tests cover the workload sizes.
 """
+import os
 import random
 
 import numpy as np
@@ -23,11 +24,14 @@ if torch.cuda.is_available():
     from tests import test_parity_causal_gqa_gpu as gq
 
 DEV = "cuda:0"
-N_CASES = 120
+# FA_RANDOM_CASES / FA_RANDOM_SEED widen the sweep (e.g. thousands of cases under another generator seed);
+# the defaults are the committed 120 cases of seed 90210.
+N_CASES = int(os.environ.get("FA_RANDOM_CASES", "120"))
+SEED = int(os.environ.get("FA_RANDOM_SEED", "90210"))
 
 
 def draw(i):
-    r = random.Random(90210 + i)
+    r = random.Random(SEED + i)
     kind = r.choice(["fwd", "fwd", "split", "bwd"])
     d = r.choice([64, 128])
     H_kv = r.choice([1, 2])
