@@ -183,26 +183,33 @@ def _oracle_task(task):
 
 
 def cpu_baseline(tasks, flops_of, budget_s, compare):
-    """Run oracle tasks in a process pool for at most ``budget_s`` seconds of wall time (after the workers
-    start). Returns (cpu_baseline record, parity record)."""
+    """Run oracle tasks in a pool of worker processes for about ``budget_s`` seconds of wall time (after the
+    workers start): at most two tasks per worker are in flight, no task is submitted once the budget is spent,
+    and the tasks in flight are finished. Returns (cpu_baseline record, parity record)."""
     import multiprocessing as mp
+    from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
     workers = max(1, min(len(os.sched_getaffinity(0)), 16))
-    ctx = mp.get_context("spawn")      # fresh interpreters: nothing of this process's GPU state is inherited
-    pool = ctx.Pool(workers, initializer=_worker_init)
-    try:
-        pool.map(abs, range(workers))  # workers up and oracle imported before the clock starts
+    # spawn: fresh interpreters, nothing of this process's GPU state is inherited
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"), initializer=_worker_init) as ex:
+        list(ex.map(abs, range(workers)))      # workers up and the oracle imported before the clock starts
         t0 = time.perf_counter()
-        done, flops, errs = 0, 0.0, []
-        for key, ref, _ in pool.imap_unordered(_oracle_task, tasks):
-            done += 1
-            flops += flops_of(key)
-            errs.extend(compare(key, ref))
-            if time.perf_counter() - t0 > budget_s:
+        done, flops, errs, nxt, pending, last_note = 0, 0.0, [], 0, set(), t0
+        while nxt < len(tasks) or pending:
+            while nxt < len(tasks) and len(pending) < 2 * workers and time.perf_counter() - t0 < budget_s:
+                pending.add(ex.submit(_oracle_task, tasks[nxt]))
+                nxt += 1
+            if not pending:
                 break
+            finished, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for fu in finished:
+                key, ref, _ = fu.result()
+                done += 1
+                flops += flops_of(key)
+                errs.extend(compare(key, ref))
+            if time.perf_counter() - last_note > 5.0:
+                last_note = time.perf_counter()
+                print(f"cpu_baseline: {done} of {len(tasks)} tasks, {last_note - t0:.1f} s", file=sys.stderr, flush=True)
         dt = time.perf_counter() - t0
-    finally:
-        pool.terminate()
-        pool.join()
     max_abs = max(e[0] for e in errs)
     rel = (sum(e[1] ** 2 for e in errs) ** 0.5) / max(sum(e[2] ** 2 for e in errs) ** 0.5, 1e-300)
     return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "cpu_model": cpu_model(),
