@@ -15,7 +15,8 @@ FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 256
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_fwd_lse", "fa_bwd", "fa_merge_states",
            "fa_fwd_split_lse", "fa_merge_lse", "fa_status_string", "fa_last_error", "fa_abi_version",
-           "fa_probe_mfma_bf16", "fa_probe_hbm_read")
+           "fa_probe_mfma_bf16", "fa_probe_hbm_read", "fa_bwd_noalloc")
+FA_NOALLOC_MAX_ROWS = 4194304
 
 _lib = None
 
@@ -40,6 +41,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_lse.restype = I
         L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
         L.fa_bwd.restype = I
+        L.fa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+        L.fa_bwd_noalloc.restype = I
         L.fa_merge_states.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, P, P]
         L.fa_merge_states.restype = I
         L.fa_fwd_split_lse.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
@@ -98,6 +101,12 @@ def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scal
            stream):
     return lib().fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype,
                         o_dtype, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype, o_dtype,
+                   stream):
+    return lib().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, in_dtype,
+                                o_dtype, stream)
 
 
 def fa_merge_states(part_m, part_l, part_o, order, num_splits, B, H, Nq, d, o, out_dtype, m_out, l_out, stream):

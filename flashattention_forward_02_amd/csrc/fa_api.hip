@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_probe.h"
 #include "fa_internal.h"
@@ -245,6 +247,111 @@ fa_status merge_impl(const char* fn, bool lse_form, const float* part_m, const f
   return launched(fn, fa::launch_merge(a, d, static_cast<hipStream_t>(stream)));
 }
 
+// ---- the built-in D buffer of fa_bwd_noalloc ----
+// D (one fp32 per query row) lives in this file-scope device array instead of a caller workspace,
+// for callers that cannot allocate device memory. Every GPU the library runs on holds its own copy
+// until the process ends; its device address is looked up once per device (hipGetSymbolAddress
+// with that device current) and the kernels receive that address. In host code the array's name is
+// not a device address and is never passed to a kernel.
+constexpr long long kScratchFloats = FA_NOALLOC_MAX_ROWS;   // 16 MiB of fp32
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to (the current device for the null
+// stream), looked up on the first call for that device.
+fa_status scratch_for_stream(const char* fn, void* stream, float** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_EHIP, "%s: cannot tell the stream's device: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_EUNSUPPORTED, "%s: device %d (at most %d devices)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = (cur >= 0 && cur != dev) ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !p)
+      return fail(FA_EHIP, "%s: device address of the built-in D buffer on device %d: %s", fn, dev,
+                  hipGetErrorString(e != hipSuccess ? e : hipErrorInvalidSymbol));
+    if (e2 != hipSuccess) return fail(FA_EHIP, "%s: restoring device %d: %s", fn, cur, hipGetErrorString(e2));
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// fa_bwd and fa_bwd_noalloc. With use_scratch the D buffer is this device's copy of `scratch`
+// (looked up after every argument check passed); otherwise it is the caller's `delta`.
+fa_status bwd_impl(const char* fn, bool use_scratch, const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv, int B, int H,
+                   int H_kv, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype,
+                   void* stream) {
+  fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
+  if (in_dtype == FA_F32) return fail(FA_EUNSUPPORTED, "%s: fp32 inputs (supported: FA_BF16, FA_F16)", fn);
+  if (o_dtype != FA_F32 && o_dtype != in_dtype)
+    return fail(FA_EINVAL, "%s: o_dtype=%d must be FA_F32 or equal to in_dtype=%d", fn, (int)o_dtype, (int)in_dtype);
+  const size_t nrows = (size_t)B * H * Nq;
+  if ((!o || !dout || !lse || (!delta && !use_scratch) || !dq) && nrows != 0)
+    return fail(FA_EINVAL, use_scratch ? "%s: o, dout, lse and dq must be non-NULL device pointers"
+                                       : "%s: o, dout, lse, delta and dq must be non-NULL device pointers", fn);
+  if (use_scratch && nrows > (size_t)kScratchFloats)
+    return fail(FA_EINVAL, "%s: B*H*Nq=%zu exceeds the %lld rows of its built-in D buffer (use fa_bwd with a caller "
+                "workspace)", fn, nrows, (long long)kScratchFloats);
+  if ((!dk || !dv) && (size_t)B * H != 0) return fail(FA_EINVAL, "%s: dk and dv must be non-NULL device pointers", fn);
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) ||
+      !aligned4(delta))
+    return fail(FA_EINVAL, "%s: o, dout, dq, dk, dv must be 16-byte and lse, delta 4-byte aligned", fn);
+  if ((size_t)B * H == 0) return FA_OK;
+  // Outputs must not overlap any input or each other (the built-in D buffer overlaps nothing).
+  const size_t qb = nrows * d * 2, kvb = (size_t)B * H_kv * Nk * d * 2, ob = nrows * d * dtype_size(o_dtype);
+  const size_t qf = nrows * d * 4, kvf = (size_t)B * H_kv * Nk * d * 4, rb = nrows * 4;
+  const void* ins[] = {q, k, v, o, dout, lse};
+  const size_t insz[] = {qb, kvb, kvb, ob, qb, rb};
+  const void* outs[] = {delta, dq, dk, dv};
+  const size_t outsz[] = {use_scratch ? 0 : rb, qf, kvf, kvf};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return fail(FA_EINVAL, "%s: an output overlaps an input", fn);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return fail(FA_EINVAL, "%s: two outputs overlap", fn);
+  }
+  if (use_scratch) {   // every argument checked: now the device is touched
+    fa_status st2 = scratch_for_stream(fn, stream, &delta);
+    if (st2 != FA_OK) return st2;
+  }
+  fa::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.causal = causal;
+  a.causal_off = Nk - Nq;
+  a.o_dtype = o_dtype;
+  a.scale = scale;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  // (Nq = 0 launches only the dK / dV kernel, which then writes zeros.)
+  return launched(fn, fa::launch_bwd(a, d, in_dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,58 +383,16 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float* delta, float* dq, float* dk, float* dv, int B, int H, int H_kv, int Nq, int Nk, int d,
                  float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
   g_last_error[0] = 0;
-  const char* fn = "fa_bwd";
-  fa_status st = check_common(fn, q, k, v, B, H, Nq, Nk, d, scale, in_dtype);
-  if (st != FA_OK) return st;
-  if ((st = check_ext(fn, H, H_kv, Nq, Nk, causal)) != FA_OK) return st;
-  if (in_dtype == FA_F32) return fail(FA_EUNSUPPORTED, "%s: fp32 inputs (supported: FA_BF16, FA_F16)", fn);
-  if (o_dtype != FA_F32 && o_dtype != in_dtype)
-    return fail(FA_EINVAL, "%s: o_dtype=%d must be FA_F32 or equal to in_dtype=%d", fn, (int)o_dtype, (int)in_dtype);
-  const size_t nrows = (size_t)B * H * Nq;
-  if ((!o || !dout || !lse || !delta || !dq) && nrows != 0)
-    return fail(FA_EINVAL, "%s: o, dout, lse, delta and dq must be non-NULL device pointers", fn);
-  if ((!dk || !dv) && (size_t)B * H != 0) return fail(FA_EINVAL, "%s: dk and dv must be non-NULL device pointers", fn);
-  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) ||
-      !aligned4(delta))
-    return fail(FA_EINVAL, "%s: o, dout, dq, dk, dv must be 16-byte and lse, delta 4-byte aligned", fn);
-  if ((size_t)B * H == 0) return FA_OK;
-  // Outputs must not overlap any input or each other.
-  const size_t qb = nrows * d * 2, kvb = (size_t)B * H_kv * Nk * d * 2, ob = nrows * d * dtype_size(o_dtype);
-  const size_t qf = nrows * d * 4, kvf = (size_t)B * H_kv * Nk * d * 4, rb = nrows * 4;
-  const void* ins[] = {q, k, v, o, dout, lse};
-  const size_t insz[] = {qb, kvb, kvb, ob, qb, rb};
-  const void* outs[] = {delta, dq, dk, dv};
-  const size_t outsz[] = {rb, qf, kvf, kvf};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return fail(FA_EINVAL, "%s: an output overlaps an input", fn);
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return fail(FA_EINVAL, "%s: two outputs overlap", fn);
-  }
-  fa::BwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.delta = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.B = B;
-  a.H = H;
-  a.H_kv = H_kv;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.causal = causal;
-  a.causal_off = Nk - Nq;
-  a.o_dtype = o_dtype;
-  a.scale = scale;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  // (Nq = 0 launches only the dK / dV kernel, which then writes zeros.)
-  return launched(fn, fa::launch_bwd(a, d, in_dtype, static_cast<hipStream_t>(stream)));
+  return bwd_impl("fa_bwd", false, q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal,
+                  in_dtype, o_dtype, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, float* dq, float* dk, float* dv, int B, int H, int H_kv, int Nq, int Nk,
+                         int d, float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+  g_last_error[0] = 0;
+  return bwd_impl("fa_bwd_noalloc", true, q, k, v, o, dout, lse, nullptr, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale,
+                  causal, in_dtype, o_dtype, stream);
 }
 
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* part_m, float* part_l, float* part_o,

@@ -156,6 +156,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and results,
+ * with no `delta` argument. D (one fp32 per query row) is kept in a buffer built into the library
+ * -- a file-scope device array of FA_NOALLOC_MAX_ROWS floats (16 MiB) that every GPU the library
+ * runs on holds until the process ends -- instead of a caller workspace. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine). Its first call on a device is its
+ * set-up: it looks up that device's copy of the buffer, and the HIP runtime loads the buffer onto
+ * the device at that point (about 18 MiB of device memory, once); later calls leave device memory
+ * as it is. A caller that must not see even that can make one call outside the region it guards.
+ *   B*H*Nq must be <= FA_NOALLOC_MAX_ROWS (FA_EINVAL otherwise; fa_bwd has no such limit).
+ * All calls on one GPU share that GPU's buffer: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give wrong gradients; calls ordered on
+ * one stream do not. D is written before it is read within every call, so nothing left by an
+ * earlier call is used. Everything else (arguments, layouts, errors) as in fa_bwd.
+ */
+#define FA_NOALLOC_MAX_ROWS 4194304
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, float* dq, float* dk, float* dv,
+                         int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                         fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
+
+/*
  * fa_fwd_split_ext -- fa_fwd_split with grouped K/V heads and an optional causal mask.
  *
  * H_kv and causal as in fa_fwd_ext; the partition and the state layouts as in fa_fwd_split.

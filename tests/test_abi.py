@@ -341,3 +341,30 @@ def test_probe_hbm_read_rejects(kw, msg):
     a.update(kw)
     assert n.fa_probe_hbm_read(**a) == n.FA_EINVAL
     assert msg in n.fa_last_error()
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=P, k=P * 2, v=P * 3, o=P * 4, dout=P * 5, lse=P * 6, dq=P * 8, dk=P * 9, dv=P * 10,
+             B=1, H=2, H_kv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, in_dtype=n.FA_BF16, o_dtype=n.FA_F32,
+             stream=None)
+    a.update(kw)
+    return n.fa_bwd_noalloc(**a)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Nq=n.FA_NOALLOC_MAX_ROWS + 1, Nk=n.FA_NOALLOC_MAX_ROWS + 1, B=1, H=1), n.FA_EINVAL, "built-in D buffer"),
+    (dict(B=2, H=2, H_kv=2, Nq=n.FA_NOALLOC_MAX_ROWS // 4 + 1, Nk=n.FA_NOALLOC_MAX_ROWS), n.FA_EINVAL,
+     "built-in D buffer"),
+    (dict(in_dtype=n.FA_F32), n.FA_EUNSUPPORTED, "fp32 inputs"),
+    (dict(dout=None), n.FA_EINVAL, "non-NULL"),
+    (dict(dq=P), n.FA_EINVAL, "overlaps an input"),
+    (dict(dk=P * 8), n.FA_EINVAL, "two outputs overlap"),
+    (dict(d=96), n.FA_EUNSUPPORTED, "d=96"),
+])
+def test_fa_bwd_noalloc_rejects_before_touching_the_device(kw, status, msg):
+    assert bwd_noalloc(**kw) == status
+    assert msg in n.fa_last_error()
+
+
+def test_fa_bwd_noalloc_empty_batch_is_ok_without_device():
+    assert bwd_noalloc(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None) == n.FA_OK
