@@ -6,12 +6,14 @@
 // row there is nothing to share between rows, so this path streams K and V once with
 // coalesced 16-byte loads and does the arithmetic on the VALU; it is bound by HBM bandwidth.
 //
-// Inside a workgroup the 256 lanes form 16 groups of 16; a group takes U keys at a time
-// (group g owns keys kbeg + g*U + 16*U*i + u), lane t of the group owns columns
-// [t*D/16, (t+1)*D/16) of q, of the K and V rows and of its accumulator. A score is D/16
-// FMAs per lane plus a butterfly over the group; each group runs the online-softmax
-// recurrence of "FlashAttention 简化版：Tiling + Online Softmax" §2.3 over its keys, and the 16
-// group states are merged at the end with the merge rule of the decoding demo.
+// Inside a workgroup the lanes form G groups of 16 (G = 16 in the 256-lane workgroups of bf16 /
+// fp16; fp32, whose one-row calls would otherwise leave a single workgroup waiting on memory
+// round trips, uses 1024 lanes, G = 64); a group takes U keys at a time (group g owns keys
+// kbeg + g*U + G*U*i + u), lane t of the group owns columns [t*D/16, (t+1)*D/16) of q, of the
+// K and V rows and of its accumulator. A score is D/16 FMAs per lane plus a butterfly over the
+// group; each group runs the online-softmax recurrence of "FlashAttention 简化版：Tiling +
+// Online Softmax" §2.3 over its keys, and the G group states are merged at the end with the
+// merge rule of the decoding demo (compensated on the fp32 path).
 //
 // fp32 inputs use s = scale * (q . k) and the accurate expf (the fp32 accuracy path);
 // bf16/fp16 inputs use base-2 scores, exp(s - m) = 2^(raw*c - m*c) with c = scale*log2(e).
@@ -82,12 +84,13 @@ __device__ __forceinline__ void store_out(void* base, size_t elem, int out_dtype
   else static_cast<_Float16*>(base)[elem] = (_Float16)x;
 }
 
-template <int D, typename T, int U>
-__global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
+template <int D, typename T, int U, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(FwdArgs a) {
   constexpr bool kAccurate = std::is_same<T, float>::value;
+  constexpr int NG = NT / 16;   // lane groups
   constexpr int DL = D / 16;  // columns per lane
-  __shared__ float sh_m[kGroups], sh_l[kGroups];
-  __shared__ float sh_o[kGroups][D];
+  __shared__ float sh_m[NG], sh_l[NG];
+  __shared__ float sh_o[NG][D];
 
   const int S = a.num_splits;
   const int split = blockIdx.x % S;
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
 #pragma unroll
   for (int c = 0; c < DL; ++c) acc[c] = comp[c] = 0.f;
 
-  for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
+  for (int base = kbeg + g * U; base < kend; base += NG * U) {
     float kx[U][DL], vx[U][DL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -180,32 +183,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
   // ---- merge the 16 group states ----
   if (t == 0) {
     sh_m[g] = m;
-    sh_l[g] = l;
+    sh_l[g] = kAccurate ? l - lcomp : l;
   }
 #pragma unroll
-  for (int c = 0; c < DL; ++c) sh_o[g][t * DL + c] = acc[c];
+  for (int c = 0; c < DL; ++c) sh_o[g][t * DL + c] = kAccurate ? acc[c] - comp[c] : acc[c];
   __syncthreads();
 
   float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kGroups; ++i) M = fmaxf(M, sh_m[i]);
-  float w[kGroups];
-  float L = 0.f;
+  for (int i = 0; i < NG; ++i) M = fmaxf(M, sh_m[i]);
+  float w[NG];
+  float L = 0.f, Lc = 0.f;
 #pragma unroll
-  for (int i = 0; i < kGroups; ++i) {
+  for (int i = 0; i < NG; ++i) {
     const float mi = sh_m[i];
     if (mi == -INFINITY) w[i] = 0.f;
     else if constexpr (kAccurate) w[i] = expf(mi - M);
     else w[i] = __builtin_amdgcn_exp2f((mi - M) * c2);
-    L = __builtin_fmaf(w[i], sh_l[i], L);
+    if constexpr (kAccurate) kahan_add(L, Lc, w[i] * sh_l[i]);   // the fp32 path merges with compensation
+    else L = __builtin_fmaf(w[i], sh_l[i], L);
   }
+  L -= Lc;
   // An empty range (possible only under the mask, in split mode) leaves M = -inf, L = 0, o = 0.
   const float m_nat = (kAccurate || M == -INFINITY) ? M : a.scale * M;
   const size_t qrow = head * a.Nq + row;
-  for (int c = tid; c < D; c += kThreads) {
-    float o = 0.f;
+  for (int c = tid; c < D; c += NT) {
+    float o = 0.f, oc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kGroups; ++i) o = __builtin_fmaf(w[i], sh_o[i][c], o);
+    for (int i = 0; i < NG; ++i) {
+      if constexpr (kAccurate) kahan_add(o, oc, w[i] * sh_o[i][c]);
+      else o = __builtin_fmaf(w[i], sh_o[i][c], o);
+    }
+    o -= oc;
     if (a.split_mode == 0) {
       store_out<T>(a.o, qrow * D + c, a.out_dtype, o / L);
     } else {
@@ -436,8 +445,11 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U>), dim3((unsigned)nwg),
-                         dim3(kThreads), kargs, 0, s);
+  // fp32 (few rows, one workgroup per row and range): 64 lane groups keep 4x the loads in flight of
+  // the 16 the memory-bound bf16 / fp16 split decode uses
+  constexpr int NT = std::is_same<T, float>::value ? 1024 : kThreads;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U, NT>), dim3((unsigned)nwg), dim3(NT),
+                         kargs, 0, s);
 }
 
 }  // namespace

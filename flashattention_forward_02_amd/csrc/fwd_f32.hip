@@ -1,30 +1,51 @@
 // Tiled FlashAttention forward for fp32 inputs (VALU, full fp32 arithmetic).
 //
 // Same recurrence as the matrix-core kernel ("FlashAttention 简化版：Tiling + Online Softmax",
-// §2.3 and §3.1), written for accuracy rather than speed: scores are s = scale * (q . k) in
-// fp32, the running max is taken on s, and exp is the accurate expf, so the result tracks the
-// float64 definition to a few fp32 ulps.
+// §2.3 and §3.1), written for accuracy: scores are s = scale * (q . k) in fp32, the running max
+// is taken on s, and exp is the accurate expf, so the result tracks the float64 definition to a
+// few fp32 ulps.
 //
-// The output accumulator and l are summed with compensation (Kahan): their sums nearly cancel
-// (|O| is small next to sum |p v| when many keys share the weight), and plain fp32 accumulation
-// over thousands of keys would lose ~sqrt(Nk) ulps of O.
+// Work decomposition. A workgroup owns 16 query rows of one (b, h) and 8 waves; each wave streams
+// its own contiguous eighth of the key range and keeps its own online-softmax state for all 16
+// rows, and the 8 states are merged at the end with the pairwise rule of "CS349E 第 11 讲
+// 01_online_softmax.py" demo 2 (the key-split of flash-decoding, inside one workgroup). So a
+// workload of few rows still spreads over many waves: 256 rows are 16 workgroups of 8 waves.
+// Inside a wave 4 adjacent lanes share a query row, each owning D/4 of its columns of q and of
+// the accumulator; a dot product is D/4 FMAs per lane plus two exchanges within the 4 lanes.
 //
-// Layout: D/32 adjacent lanes share one query row, each owning 32 of its columns of q and of
-// the output accumulator; a dot product is 32 FMAs per lane plus a butterfly over those lanes.
-// Key/value tiles of 32 rows are staged in LDS (every lane of a wave reads the same K/V row at
-// the same time, so the reads are broadcasts).
+// K/V tiles go from HBM straight into a per-wave LDS region (direct-to-LDS loads, two buffers,
+// the next tile in flight while the current one is used), so the key loop needs no workgroup
+// barrier. Every lane of a wave reads the same key row at the same time (16 rows x 4 column
+// slices), so the LDS reads are broadcasts.
+//
+// Accuracy of the sums. O's sum sum_j p_j v_j nearly cancels (|O| is small next to
+// sum |p v| when many keys share the weight), so plain fp32 accumulation over thousands of keys
+// would lose ~sqrt(Nk) ulps. Each tile's contribution (16 or 8 keys) is summed plainly and then
+// added to the running l and accumulator with compensation (Kahan), and the merge of the 8 wave
+// states is compensated too: the error grows with the tile length, not with Nk.
 
 #include "fa_internal.h"
+#include "mfma_common.h"
 
 namespace fa {
 namespace {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+constexpr int kWavesF = 8;
+constexpr int kThreadsF = kWavesF * 64;
+constexpr int kLPR = 4;              // lanes per query row
+constexpr int kRows = 64 / kLPR;     // query rows per workgroup (every wave holds all of them)
 
-constexpr int kThreads = 256;
-constexpr int kBCF = 32;  // keys per tile
+template <int D>
+struct F32Cfg {
+  static constexpr int DPL = D / kLPR;                  // columns per lane
+  static constexpr int KT = D == 64 ? 16 : 8;           // keys per tile
+  static constexpr int TILE = KT * D;                   // floats per K (or V) tile
+  static constexpr int LOADS = TILE / 4 / 64;           // 16-byte direct-to-LDS loads per lane per tensor
+  static_assert(LOADS * 4 * 64 == TILE, "tile / wave mismatch");
+  static constexpr int WAVE_BUF = 2 * TILE;             // floats per wave and buffer: K then V
+};
 
-// sum += x with the rounding error carried in comp (Kahan).
+// sum += x with the rounding error carried in comp (Kahan): the compensated value is sum - comp.
 __device__ __forceinline__ void kahan_add(float& sum, float& comp, float x) {
   const float y = x - comp;
   const float t = sum + y;
@@ -32,22 +53,36 @@ __device__ __forceinline__ void kahan_add(float& sum, float& comp, float x) {
   sum = t;
 }
 
-// sum += p * v, the product rounded once into the compensated sum.
-__device__ __forceinline__ void kahan_fma(float& sum, float& comp, float p, float v) {
-  const float y = __builtin_fmaf(p, v, -comp);
-  const float t = sum + y;
-  comp = (t - sum) - y;
-  sum = t;
+// Sum of x over the 4 lanes of a query row (DPP quad permutes: swap neighbours, then pairs).
+__device__ __forceinline__ float row_sum4(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
+// HBM -> LDS of keys [key0, key0 + KT) of one tensor (rows past kend repeat row kend - 1; their
+// scores are masked). Row-major [KT][D] in LDS.
+template <int D>
+__device__ __forceinline__ void load_tile_f32(const float* __restrict__ X, float* lx, int key0, int kend, int lane) {
+  typedef F32Cfg<D> C;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int c = i * 64 + lane;            // 16-byte chunk of the tile
+    const int r = c / (D / 4);
+    const int key = min(key0 + r, kend - 1);
+    global_to_lds16(X + (size_t)key * D + (c % (D / 4)) * 4, &lx[i * 256]);
+  }
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
-  constexpr int LPR = D / 32;               // lanes per query row
-  constexpr int ROWS = kThreads / LPR;      // query rows per workgroup
-  constexpr int LOADS = kBCF * D / 4 / kThreads;
-  static_assert(LOADS * 4 * kThreads == kBCF * D, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) float ks[kBCF * D];
-  __shared__ __attribute__((aligned(16))) float vs[kBCF * D];
+__global__ __launch_bounds__(kThreadsF) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
+  typedef F32Cfg<D> C;
+  constexpr int DPL = C::DPL, KT = C::KT;
+  // The two tile buffers are separate objects, and the key loop steps two tiles at a time, so the
+  // compiler sees that a step's reads do not alias the loads of the next tile in flight (it would
+  // otherwise wait for those loads before the first read).
+  __shared__ __attribute__((aligned(16))) float lds0[kWavesF * C::WAVE_BUF];
+  __shared__ __attribute__((aligned(16))) float lds1[kWavesF * C::WAVE_BUF];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = wg % n_qtiles;
@@ -65,116 +100,176 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
   int kend = split_begin(split + 1, a.Nk, a.num_splits);
 
   const int tid = threadIdx.x;
-  const int row = qt * ROWS + tid / LPR;
-  const int col0 = (tid % LPR) * 32;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rloc = lane / kLPR;
+  const int row = qt * kRows + rloc;
+  const int col0 = (lane % kLPR) * DPL;
   const bool live = row < a.Nq;
-  // Causal mask: this row sees keys < row_end; the workgroup stops after the last key any of
-  // its rows sees (key tiles wholly past it are skipped).
+  // Causal mask: this row sees keys < row_end; the workgroup's range ends after the last key its
+  // last row sees (key tiles wholly past it are skipped).
   int row_end = kend;
   if (a.causal) {
     row_end = min(kend, row + a.causal_off + 1);
-    kend = min(kend, min(a.Nq, (qt + 1) * ROWS) - 1 + a.causal_off + 1);
+    kend = min(kend, min(a.Nq, (qt + 1) * kRows) + a.causal_off);
   }
+  // This wave's share of the range: contiguous, in whole tiles.
+  const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  const int t0 = (int)(((long long)wave * ntiles) / kWavesF);
+  const int t1 = (int)(((long long)(wave + 1) * ntiles) / kWavesF);
 
-  float q[32], acc[32], comp[32];
+  float q[DPL], acc[DPL], comp[DPL], tacc[DPL];
 #pragma unroll
-  for (int c = 0; c < 32; c += 4) {
+  for (int c = 0; c < DPL; c += 4) {
     f32x4_t x = {0.f, 0.f, 0.f, 0.f};
     if (live) x = *reinterpret_cast<const f32x4_t*>(Q + (size_t)row * D + col0 + c);
-    q[c] = x[0]; q[c + 1] = x[1]; q[c + 2] = x[2]; q[c + 3] = x[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[c + i] = comp[c + i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      q[c + i] = x[i];
+      acc[c + i] = comp[c + i] = 0.f;
+    }
   }
   float m = -INFINITY, l = 0.f, lcomp = 0.f;
 
-  for (int key0 = kbeg; key0 < kend; key0 += kBCF) {
-    const int nvalid = min(kBCF, kend - key0);
-    __syncthreads();  // the previous tile is consumed
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = (tid + i * kThreads) * 4;
-      const int r = e / D;
-      f32x4_t kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (r < nvalid) {
-        kx = *reinterpret_cast<const f32x4_t*>(K + (size_t)(key0 + r) * D + (e % D));
-        vx = *reinterpret_cast<const f32x4_t*>(V + (size_t)(key0 + r) * D + (e % D));
-      }
-      *reinterpret_cast<f32x4_t*>(&ks[e]) = kx;
-      *reinterpret_cast<f32x4_t*>(&vs[e]) = vx;
+  float* w0 = lds0 + wave * C::WAVE_BUF;    // [K, V][TILE]
+  float* w1 = lds1 + wave * C::WAVE_BUF;
+  // One tile: wait for it, start the next one into the other buffer, then the online-softmax update.
+  auto step = [&](int t, float* cur, float* nxt) {
+    const int key0 = kbeg + t * KT;
+    const float* lk = cur;
+    const float* lv = cur + C::TILE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile has landed (this wave's own loads)
+    if (t + 1 < t1) {
+      load_tile_f32<D>(K, nxt, key0 + KT, kend, lane);
+      load_tile_f32<D>(V, nxt + C::TILE, key0 + KT, kend, lane);
     }
-    __syncthreads();
-
-    float s[kBCF];
-    float mx = -INFINITY;
+    float s[KT];
+    float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kBCF; ++j) {
+    for (int j = 0; j < KT; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < 32; c += 4) {
-        const f32x4_t kx = *reinterpret_cast<const f32x4_t*>(&ks[j * D + col0 + c]);
+      for (int c = 0; c < DPL; c += 4) {
+        const f32x4_t kx = *reinterpret_cast<const f32x4_t*>(&lk[j * D + col0 + c]);
         dot = __builtin_fmaf(q[c], kx[0], dot);
         dot = __builtin_fmaf(q[c + 1], kx[1], dot);
         dot = __builtin_fmaf(q[c + 2], kx[2], dot);
         dot = __builtin_fmaf(q[c + 3], kx[3], dot);
       }
-#pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) dot += __shfl_xor(dot, off);
+      dot = row_sum4(dot);
       s[j] = (key0 + j < row_end) ? a.scale * dot : -INFINITY;
-      mx = fmaxf(mx, s[j]);
+      mt = fmaxf(mt, s[j]);
     }
-    const float mnew = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
+    const float mnew = fmaxf(m, mt);
+    if (mnew != -INFINITY) {               // a tile with no visible key for this row leaves its state alone
+      if (mnew != m) {                     // the max grew: rescale l and the accumulator by exp(m_old - m_new)
+        const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
+        l *= alpha;
+        lcomp *= alpha;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      acc[c] *= alpha;
-      comp[c] *= alpha;
-    }
-    l *= alpha;
-    lcomp *= alpha;
-#pragma unroll
-    for (int j = 0; j < kBCF; ++j) {
-      const float p = (key0 + j < row_end) ? expf(s[j] - mnew) : 0.f;
-      kahan_add(l, lcomp, p);
-#pragma unroll
-      for (int c = 0; c < 32; c += 4) {
-        const f32x4_t vx = *reinterpret_cast<const f32x4_t*>(&vs[j * D + col0 + c]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kahan_fma(acc[c + i], comp[c + i], p, vx[i]);
+        for (int c = 0; c < DPL; ++c) {
+          acc[c] *= alpha;
+          comp[c] *= alpha;
+        }
+        m = mnew;
       }
-    }
-    m = mnew;
-  }
-
-  if (!live) return;
-  if (a.split_mode == 0) {
-    const float inv = 1.f / l;
-    float* O = static_cast<float*>(a.o) + (head * (size_t)a.Nq + row) * D + col0;
+      float tl = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; c += 4) {
-      f32x4_t x = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
-      *reinterpret_cast<f32x4_t*>(O + c) = x;
+      for (int c = 0; c < DPL; ++c) tacc[c] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        const float p = (key0 + j < row_end) ? expf(s[j] - m) : 0.f;
+        tl += p;
+#pragma unroll
+        for (int c = 0; c < DPL; c += 4) {
+          const f32x4_t vx = *reinterpret_cast<const f32x4_t*>(&lv[j * D + col0 + c]);
+          tacc[c] = __builtin_fmaf(p, vx[0], tacc[c]);
+          tacc[c + 1] = __builtin_fmaf(p, vx[1], tacc[c + 1]);
+          tacc[c + 2] = __builtin_fmaf(p, vx[2], tacc[c + 2]);
+          tacc[c + 3] = __builtin_fmaf(p, vx[3], tacc[c + 3]);
+        }
+      }
+      kahan_add(l, lcomp, tl);
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) kahan_add(acc[c], comp[c], tacc[c]);
     }
-    if (col0 == 0) {
-      if (a.m_out) a.m_out[head * a.Nq + row] = m;
-      if (a.l_out) a.l_out[head * a.Nq + row] = l;
-      if (a.lse_out) a.lse_out[head * a.Nq + row] = m + logf(l);
+  };
+  if (t0 < t1) {
+    load_tile_f32<D>(K, w0, kbeg + t0 * KT, kend, lane);
+    load_tile_f32<D>(V, w0 + C::TILE, kbeg + t0 * KT, kend, lane);
+  }
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    step(t, w0, w1);
+    step(t + 1, w1, w0);
+  }
+  if (t < t1) step(t, w0, w1);
+
+  // ---- merge the 8 wave states of every row (compensated), then the epilogue ----
+  __syncthreads();                         // every wave is done with its tiles: the LDS is reused
+  // per wave: m[16], l[16], then the 16 x D compensated accumulator; waves 0-3 in lds0, 4-7 in lds1
+  constexpr int WSTATE = 2 * kRows + kRows * D;
+  static_assert(4 * WSTATE <= kWavesF * C::WAVE_BUF, "merge state does not fit");
+  float* st = (wave < 4 ? lds0 : lds1) + (wave & 3) * WSTATE;
+  if (lane % kLPR == 0) {
+    st[rloc] = m;
+    st[kRows + rloc] = l - lcomp;
+  }
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) st[2 * kRows + rloc * D + col0 + c] = acc[c] - comp[c];
+  __syncthreads();
+
+  // thread -> (row r, 16-column slice): D / 32 x ... columns per thread
+  constexpr int CPT = D * kRows / kThreadsF;   // columns per thread (2 or 4)
+  const int r = tid / (D / CPT);
+  const int cc = (tid % (D / CPT)) * CPT;
+  const int grow = qt * kRows + r;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWavesF; ++w) M = fmaxf(M, (w < 4 ? lds0 : lds1)[(w & 3) * WSTATE + r]);
+  float L = 0.f, Lc = 0.f, o[CPT], oc[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) o[i] = oc[i] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWavesF; ++w) {
+      const float* ws = (w < 4 ? lds0 : lds1) + (w & 3) * WSTATE;
+      const float mw = ws[r];
+      if (mw == -INFINITY) continue;      // a wave that saw no key of this row weighs 0
+      const float wgt = expf(mw - M);
+      kahan_add(L, Lc, wgt * ws[kRows + r]);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) kahan_add(o[i], oc[i], wgt * ws[2 * kRows + r * D + cc + i]);
+    }
+  }
+  L -= Lc;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) o[i] -= oc[i];
+  if (grow >= a.Nq) return;
+
+  if (a.split_mode == 0) {
+    const float inv = 1.f / L;
+    float* O = static_cast<float*>(a.o) + (head * (size_t)a.Nq + grow) * D + cc;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) O[i] = o[i] * inv;
+    if (cc == 0) {
+      if (a.m_out) a.m_out[head * a.Nq + grow] = M;
+      if (a.l_out) a.l_out[head * a.Nq + grow] = L;
+      if (a.lse_out) a.lse_out[head * a.Nq + grow] = M + logf(L);
     }
   } else {
-    const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + row;
-    float* P = a.part_o + prow * D + col0;
+    const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + grow;
+    float* P = a.part_o + prow * D + cc;
     // (lse, o / l) form: a row with no key in this range keeps (-inf, 0)
-    const float w = (a.split_mode == 2) ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
+    const float w = (a.split_mode == 2) ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
 #pragma unroll
-    for (int c = 0; c < 32; c += 4) {
-      f32x4_t x = {acc[c] * w, acc[c + 1] * w, acc[c + 2] * w, acc[c + 3] * w};
-      *reinterpret_cast<f32x4_t*>(P + c) = x;
-    }
-    if (col0 == 0) {
+    for (int i = 0; i < CPT; ++i) P[i] = o[i] * w;
+    if (cc == 0) {
       if (a.split_mode == 2) {
-        a.part_m[prow] = (m == -INFINITY) ? -INFINITY : m + logf(l);
+        a.part_m[prow] = (M == -INFINITY) ? -INFINITY : M + logf(L);
       } else {
-        a.part_m[prow] = m;
-        a.part_l[prow] = l;
+        a.part_m[prow] = M;
+        a.part_l[prow] = L;
       }
     }
   }
@@ -182,14 +277,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qtil
 
 template <int D>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
-  constexpr int ROWS = kThreads / (D / 32);
-  const int n_qtiles = (a.Nq + ROWS - 1) / ROWS;
+  const int n_qtiles = (a.Nq + kRows - 1) / kRows;
   const long long nwg = (long long)n_qtiles * a.num_splits * a.H * a.B;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   int nq = n_qtiles;
   void* kargs[] = {&args, &nq};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f32_kernel<D>), dim3((unsigned)nwg), dim3(kThreads),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f32_kernel<D>), dim3((unsigned)nwg), dim3(kThreadsF),
                          kargs, 0, s);
 }
 
