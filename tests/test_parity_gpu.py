@@ -353,7 +353,8 @@ def test_merge_of_all_empty_parts_gives_zero(d):
 
 
 def test_decode_bf16_full_size_split16_shuffled_merge():
-    """B=16, H=32, one query, Nk=32768, d=128 bf16; 16 splits merged in default_rng(5).permutation(16) order."""
+    """B=16, H=32, one query, Nk=32768, d=128 bf16; 16 splits merged in default_rng(5).permutation(16) order;
+    64 whole heads against the oracle."""
     w = si.DECODE_BF16
     say("decode: generating inputs on the device")
     q, k, v = si.decode_inputs_device(w, DEV)
@@ -366,8 +367,9 @@ def test_decode_bf16_full_size_split16_shuffled_merge():
     o, m, l, o_seq = (si.torch_to_f64(x) for x in (o, m, l, o_seq))
     assert np.all(np.isfinite(o))
     assert np.max(np.abs(o - o_seq)) < 1e-5
+    # 64 of the 512 heads: every batch entry four times, heads drawn without replacement per entry
     rng = np.random.default_rng(55)
-    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 12), rng.integers(0, w.H, 12))]
+    heads = [(b, int(h)) for b in range(w.B) for h in rng.choice(w.H, 4, replace=False)]
     got, ref, gm, gl, rm, rl, bd = [], [], [], [], [], [], []
     for b, h in heads:
         qh, kh, vh = (si.torch_to_f64(x[b, h]) for x in (q, k, v))
