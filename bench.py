@@ -280,6 +280,36 @@ def run_probes(torch, fa, stream):
 # main
 # ---------------------------------------------------------------------------
 
+def time_split_one_query(torch, fa, q, k, v, o_ref, scale, stream, S=16, calls=200):
+    """The single query the split-KV way: S key ranges on S workgroups, then the merge.
+
+    fa_fwd keeps one row on one workgroup (it takes no workspace), so its time is set by one compute
+    unit's load rate; the decoding demo's blocks of 256 keys as 16 ranges spread the row over 16."""
+    part_lse = torch.empty((S,) + tuple(q.shape[:3]), device=q.device, dtype=torch.float32)
+    part_o = torch.empty((S,) + tuple(q.shape), device=q.device, dtype=torch.float32)
+    o = torch.empty_like(o_ref)
+
+    def call():
+        fa.fwd_split_lse(q, k, v, S, scale=scale, workspace=(part_lse, part_o))
+        fa.merge_lse(part_lse, part_o, out=o, return_lse=False)
+
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / calls * 1e3)
+    return {"us_per_call": best, "num_splits": S, "max_abs_diff_vs_fa_fwd": (o - o_ref).abs().max().item(),
+            "what": f"fa_fwd_split_lse over {S} key ranges of {k.shape[2] // S} keys, then "
+                    f"fa_merge_lse; best of 3 runs of {calls} back-to-back calls"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -471,10 +501,12 @@ def main():
             result.update({"metric": f"FA fwd microseconds per call at {what}", "unit": "us",
                            "value": ms_per_step * 1e3, "higher_is_better": False, "config": cfg,
                            "tflops": tflops})
-            kname = "decode_kernel" if wname == "one_query" else "fwd_f32_kernel"
+            kname = "fwd_f32_rows_kernel" if wname == "one_query" else "fwd_f32_kernel"
             result["roofline"] = {"bound": "alu", "kernel": kname, "achieved": achieved,
                                   "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, **launch_stats, "traffic": None}
+            if wname == "one_query":
+                result["split_path"] = time_split_one_query(torch, fa, q, k, v, o, wl.scale, stream)
         elif wname == "batched_queries":
             result.update({"metric": "FA fwd TFLOP/s (4*Nq*Nk*d) at 4096 queries sharing Nk=4096 keys, d=64 fp32; "
                                      "% of fp32 vector peak", "unit": "TFLOP/s", "value": tflops, "config": cfg})

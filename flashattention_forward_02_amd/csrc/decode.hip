@@ -6,17 +6,15 @@
 // row there is nothing to share between rows, so this path streams K and V once with
 // coalesced 16-byte loads and does the arithmetic on the VALU; it is bound by HBM bandwidth.
 //
-// Inside a workgroup the lanes form G groups of 16 (G = 16 in the 256-lane workgroups of bf16 /
-// fp16; fp32, whose one-row calls would otherwise leave a single workgroup waiting on memory
-// round trips, uses 1024 lanes, G = 64); a group takes U keys at a time (group g owns keys
-// kbeg + g*U + G*U*i + u), lane t of the group owns columns [t*D/16, (t+1)*D/16) of q, of the
-// K and V rows and of its accumulator. A score is D/16 FMAs per lane plus a butterfly over the
-// group; each group runs the online-softmax recurrence of "FlashAttention 简化版：Tiling +
-// Online Softmax" §2.3 over its keys, and the G group states are merged at the end with the
-// merge rule of the decoding demo (compensated on the fp32 path).
+// Inside a workgroup the 256 lanes form 16 groups of 16; a group takes U keys at a time (group g
+// owns keys kbeg + g*U + 16*U*i + u), lane t of the group owns columns [t*D/16, (t+1)*D/16) of q,
+// of the K and V rows and of its accumulator. A score is D/16 FMAs per lane plus a butterfly over
+// the group; each group runs the online-softmax recurrence of "FlashAttention 简化版：Tiling +
+// Online Softmax" §2.3 over its keys, and the 16 group states are merged at the end with the merge
+// rule of the decoding demo.
 //
-// fp32 inputs use s = scale * (q . k) and the accurate expf (the fp32 accuracy path);
-// bf16/fp16 inputs use base-2 scores, exp(s - m) = 2^(raw*c - m*c) with c = scale*log2(e).
+// These kernels take bf16 / fp16 inputs and use base-2 scores, exp(s - m) = 2^(raw*c - m*c) with
+// c = scale*log2(e); fp32 rows go to the fp32 kernels.
 
 #include <type_traits>
 
@@ -31,50 +29,28 @@ constexpr int kGroups = kThreads / 16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
-// Load N consecutive elements of T and widen them to fp32.
+// Load N consecutive bf16 / fp16 elements and widen them to fp32.
 template <typename T, int N>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[N]) {
-  if constexpr (std::is_same<T, float>::value) {
-    static_assert(N % 4 == 0, "");
-#pragma unroll
-    for (int i = 0; i < N; i += 4) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p + i);
-      out[i] = __uint_as_float(x[0]);
-      out[i + 1] = __uint_as_float(x[1]);
-      out[i + 2] = __uint_as_float(x[2]);
-      out[i + 3] = __uint_as_float(x[3]);
-    }
+  static_assert(N == 4 || N == 8, "");
+  unsigned w[N / 2];
+  if constexpr (N == 8) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
   } else {
-    static_assert(N == 4 || N == 8, "");
-    unsigned w[N / 2];
-    if constexpr (N == 8) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
-      w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
-    } else {
-      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
-      w[0] = x[0]; w[1] = x[1];
-    }
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    w[0] = x[0]; w[1] = x[1];
+  }
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      if constexpr (std::is_same<T, __bf16>::value) {
-        out[2 * i] = __uint_as_float(w[i] << 16);
-        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      } else {
-        out[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xffffu));
-        out[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
-      }
+  for (int i = 0; i < N / 2; ++i) {
+    if constexpr (std::is_same<T, __bf16>::value) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      out[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xffffu));
+      out[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
     }
   }
-}
-
-// sum += x with the rounding error carried in comp (Kahan); used on the fp32 path, where many keys
-// share the weight and plain fp32 accumulation would lose ~sqrt(Nk) ulps of the nearly
-// cancelling sum p v.
-__device__ __forceinline__ void kahan_add(float& sum, float& comp, float x) {
-  const float y = x - comp;
-  const float t = sum + y;
-  comp = (t - sum) - y;
-  sum = t;
 }
 
 template <typename T>
@@ -84,10 +60,9 @@ __device__ __forceinline__ void store_out(void* base, size_t elem, int out_dtype
   else static_cast<_Float16*>(base)[elem] = (_Float16)x;
 }
 
-template <int D, typename T, int U, int NT>
-__global__ __launch_bounds__(NT) void decode_kernel(FwdArgs a) {
-  constexpr bool kAccurate = std::is_same<T, float>::value;
-  constexpr int NG = NT / 16;   // lane groups
+template <int D, typename T, int U>
+__global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
+  constexpr int NG = kGroups;
   constexpr int DL = D / 16;  // columns per lane
   __shared__ float sh_m[NG], sh_l[NG];
   __shared__ float sh_o[NG][D];
@@ -114,9 +89,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(FwdArgs a) {
   load_row<T, DL>(Qr, q);
   const float c2 = a.scale_log2e;
 
-  float m = -INFINITY, l = 0.f, lcomp = 0.f, acc[DL], comp[DL];
+  float m = -INFINITY, l = 0.f, acc[DL];
 #pragma unroll
-  for (int c = 0; c < DL; ++c) acc[c] = comp[c] = 0.f;
+  for (int c = 0; c < DL; ++c) acc[c] = 0.f;
 
   for (int base = kbeg + g * U; base < kend; base += NG * U) {
     float kx[U][DL], vx[U][DL];
@@ -141,41 +116,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(FwdArgs a) {
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) dot += __shfl_xor(dot, off);
       const bool ok = base + u < kend;
-      s[u] = ok ? (kAccurate ? a.scale * dot : dot) : -INFINITY;
+      s[u] = ok ? dot : -INFINITY;
       mx = fmaxf(mx, s[u]);
     }
     const float mnew = fmaxf(m, mx);
-    float alpha;
-    if constexpr (kAccurate) alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
-    else alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c2);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c2);
     l *= alpha;
 #pragma unroll
     for (int c = 0; c < DL; ++c) acc[c] *= alpha;
-    if constexpr (kAccurate) {
-      lcomp *= alpha;
-#pragma unroll
-      for (int c = 0; c < DL; ++c) comp[c] *= alpha;
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float p;
-      if constexpr (kAccurate) p = expf(s[u] - mnew);
-      else p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u], c2, -mnew * c2));
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u], c2, -mnew * c2));
       if (s[u] == -INFINITY) p = 0.f;
-      if constexpr (kAccurate) {
-        kahan_add(l, lcomp, p);
+      l += p;
 #pragma unroll
-        for (int c = 0; c < DL; ++c) {
-          const float y = __builtin_fmaf(p, vx[u][c], -comp[c]);
-          const float t2 = acc[c] + y;
-          comp[c] = (t2 - acc[c]) - y;
-          acc[c] = t2;
-        }
-      } else {
-        l += p;
-#pragma unroll
-        for (int c = 0; c < DL; ++c) acc[c] = __builtin_fmaf(p, vx[u][c], acc[c]);
-      }
+      for (int c = 0; c < DL; ++c) acc[c] = __builtin_fmaf(p, vx[u][c], acc[c]);
     }
     m = mnew;
   }
@@ -183,38 +138,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(FwdArgs a) {
   // ---- merge the 16 group states ----
   if (t == 0) {
     sh_m[g] = m;
-    sh_l[g] = kAccurate ? l - lcomp : l;
+    sh_l[g] = l;
   }
 #pragma unroll
-  for (int c = 0; c < DL; ++c) sh_o[g][t * DL + c] = kAccurate ? acc[c] - comp[c] : acc[c];
+  for (int c = 0; c < DL; ++c) sh_o[g][t * DL + c] = acc[c];
   __syncthreads();
 
   float M = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NG; ++i) M = fmaxf(M, sh_m[i]);
   float w[NG];
-  float L = 0.f, Lc = 0.f;
+  float L = 0.f;
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const float mi = sh_m[i];
-    if (mi == -INFINITY) w[i] = 0.f;
-    else if constexpr (kAccurate) w[i] = expf(mi - M);
-    else w[i] = __builtin_amdgcn_exp2f((mi - M) * c2);
-    if constexpr (kAccurate) kahan_add(L, Lc, w[i] * sh_l[i]);   // the fp32 path merges with compensation
-    else L = __builtin_fmaf(w[i], sh_l[i], L);
+    w[i] = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mi - M) * c2);
+    L = __builtin_fmaf(w[i], sh_l[i], L);
   }
-  L -= Lc;
   // An empty range (possible only under the mask, in split mode) leaves M = -inf, L = 0, o = 0.
-  const float m_nat = (kAccurate || M == -INFINITY) ? M : a.scale * M;
+  const float m_nat = (M == -INFINITY) ? M : a.scale * M;
   const size_t qrow = head * a.Nq + row;
-  for (int c = tid; c < D; c += NT) {
-    float o = 0.f, oc = 0.f;
+  for (int c = tid; c < D; c += kThreads) {
+    float o = 0.f;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if constexpr (kAccurate) kahan_add(o, oc, w[i] * sh_o[i][c]);
-      else o = __builtin_fmaf(w[i], sh_o[i][c], o);
-    }
-    o -= oc;
+    for (int i = 0; i < NG; ++i) o = __builtin_fmaf(w[i], sh_o[i][c], o);
     if (a.split_mode == 0) {
       store_out<T>(a.o, qrow * D + c, a.out_dtype, o / L);
     } else {
@@ -419,46 +366,38 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   constexpr int U = (D == 64) ? 8 : 4;
   // Rows that share K and V go to decode_rows_kernel: without the mask (or with one row, which
   // sees every key) the G * Nq rows of each K/V head, viewed as one head.
-  if constexpr (!std::is_same<T, float>::value) {
-    if (!a.causal || a.Nq == 1) {
-      FwdArgs v = a;
-      v.H = a.H_kv;
-      v.Nq = (a.H / a.H_kv) * a.Nq;
-      v.causal = 0;
-      if (v.Nq >= 2) {
-        const bool r4 = v.Nq >= 3;
-        const int R = r4 ? 4 : 2;
-        const long long nwg = (long long)a.num_splits * ((v.Nq + R - 1) / R) * v.H * v.B;
-        if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        void* kargs[] = {&v};
-        // one or two keys per group step: the R-row states take the registers, and more waves
-        // in flight keep more loads in flight (d = 128, R = 4: 1 key 0.386 ms, 2 keys 0.389,
-        // 4 keys 0.50, 8 keys 0.67 on the grouped decode workload)
-        constexpr int UR = (D == 128) ? 1 : 2;
-        const void* k = r4 ? reinterpret_cast<const void*>(&decode_rows_kernel<D, T, UR, 4>)
-                           : reinterpret_cast<const void*>(&decode_rows_kernel<D, T, UR, 2>);
-        return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
-      }
+  if (!a.causal || a.Nq == 1) {
+    FwdArgs v = a;
+    v.H = a.H_kv;
+    v.Nq = (a.H / a.H_kv) * a.Nq;
+    v.causal = 0;
+    if (v.Nq >= 2) {
+      const bool r4 = v.Nq >= 3;
+      const int R = r4 ? 4 : 2;
+      const long long nwg = (long long)a.num_splits * ((v.Nq + R - 1) / R) * v.H * v.B;
+      if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      void* kargs[] = {&v};
+      // one or two keys per group step: the R-row states take the registers, and more waves
+      // in flight keep more loads in flight (d = 128, R = 4: 1 key 0.386 ms, 2 keys 0.389,
+      // 4 keys 0.50, 8 keys 0.67 on the grouped decode workload)
+      constexpr int UR = (D == 128) ? 1 : 2;
+      const void* k = r4 ? reinterpret_cast<const void*>(&decode_rows_kernel<D, T, UR, 4>)
+                         : reinterpret_cast<const void*>(&decode_rows_kernel<D, T, UR, 2>);
+      return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
     }
   }
   const long long nwg = (long long)a.num_splits * a.Nq * a.H * a.B;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  // fp32 (few rows, one workgroup per row and range): 64 lane groups keep 4x the loads in flight of
-  // the 16 the memory-bound bf16 / fp16 split decode uses
-  constexpr int NT = std::is_same<T, float>::value ? 1024 : kThreads;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U, NT>), dim3((unsigned)nwg), dim3(NT),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U>), dim3((unsigned)nwg), dim3(kThreads),
                          kargs, 0, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s) {
-  if (in_dtype == kF32) {
-    if (d == 64) return launch_typed<64, float>(a, s);
-    if (d == 128) return launch_typed<128, float>(a, s);
-  } else if (in_dtype == kBF16) {
+  if (in_dtype == kBF16) {
     if (d == 64) return launch_typed<64, __bf16>(a, s);
     if (d == 128) return launch_typed<128, __bf16>(a, s);
   } else if (in_dtype == kF16) {

@@ -148,8 +148,8 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
   a.out_dtype = out_dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
-  else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
+  if (in_dtype == FA_F32) e = Nq <= fa::kDecodeMaxNq ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
+  else if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
   return launched(fn, e);
 }
@@ -187,8 +187,8 @@ fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const voi
   a.split_mode = lse_form ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
-  else if (in_dtype == FA_F32) e = fa::launch_fwd_f32(a, d, s);
+  if (in_dtype == FA_F32) e = Nq <= fa::kDecodeMaxNq ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
+  else if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
   return launched(fn, e);
 }

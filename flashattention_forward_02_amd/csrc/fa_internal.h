@@ -89,6 +89,7 @@ struct BwdArgs {
 hipError_t launch_fwd_mfma(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_f32_rows(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t s);
 hipError_t launch_probe_mfma(float* out, int nblocks, int iters, hipStream_t s);

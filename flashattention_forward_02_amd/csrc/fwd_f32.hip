@@ -23,6 +23,9 @@
 // would lose ~sqrt(Nk) ulps. Each tile's contribution (16 or 8 keys) is summed plainly and then
 // added to the running l and accumulator with compensation (Kahan), and the merge of the 8 wave
 // states is compensated too: the error grows with the tile length, not with Nk.
+//
+// Up to 16 query rows go to fwd_f32_rows_kernel instead (one workgroup per key range, row and
+// head, keys spread over the lanes; described above the kernel).
 
 #include "fa_internal.h"
 #include "mfma_common.h"
@@ -275,6 +278,221 @@ __global__ __launch_bounds__(kThreadsF) void fwd_f32_kernel(FwdArgs a, int n_qti
   }
 }
 
+// ---- few query rows (Nq <= 16): one workgroup per (key range, row, head), keys across lanes ----
+// With one row per workgroup there is nothing to share through LDS, and the time goes to memory
+// round trips, not arithmetic. So the roles of rows and keys swap inside a wave: the wave holds
+// the one query row, and each group of LPK lanes (CPL columns each) takes a different key, so a
+// key costs its group CPL FMAs, a short exchange and one expf. K and V go straight into registers,
+// P steps ahead of their use, in 16 waves: about 256 KiB in flight per workgroup. Step i of wave
+// w covers keys kbeg + (i * NW + w) * G + [0, G), so the waves walk the range together. Each group
+// keeps its own (m, l, acc), summed plainly over 8 steps and then added with compensation; the
+// groups of a wave are merged, then the waves (all compensated).
+template <int D>
+struct F32RowCfg {
+  static constexpr int CPL = 8;           // columns per lane
+  static constexpr int LPK = D / CPL;     // lanes per key: 8 (d = 64) or 16 (d = 128)
+  static constexpr int G = 64 / LPK;      // keys per wave step
+  static constexpr int NW = 16;           // waves per workgroup
+  static constexpr int P = 4;             // steps in flight per wave
+};
+constexpr int kThreadsRows = F32RowCfg<64>::NW * 64;
+
+// Sum over the LPK lanes of a key group (DPP: neighbours, pairs, then mirrored halves).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  if constexpr (LPK == 16)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+
+// Lane j of a group owns columns r * 4 * LPK + 4 j + [0, 4) for r < CPL / 4, so one 16-byte load
+// instruction of the wave covers whole contiguous row segments.
+template <int D>
+__device__ __forceinline__ void load_key_cols(const float* __restrict__ row, int j, float (&x)[F32RowCfg<D>::CPL]) {
+  typedef F32RowCfg<D> C;
+#pragma unroll
+  for (int r = 0; r < C::CPL / 4; ++r) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + r * 4 * C::LPK + 4 * j);
+    x[4 * r] = v[0];
+    x[4 * r + 1] = v[1];
+    x[4 * r + 2] = v[2];
+    x[4 * r + 3] = v[3];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreadsRows) void fwd_f32_rows_kernel(FwdArgs a) {
+  typedef F32RowCfg<D> C;
+  constexpr int CPL = C::CPL, LPK = C::LPK, G = C::G, NW = C::NW, P = C::P;
+  // merge state: per wave m[G], l[G], acc[G][D], then per wave (m, l, o[D])
+  constexpr int WSTATE = 2 * G + G * D;
+  __shared__ float st_all[NW * WSTATE];
+
+  const int S = a.num_splits;
+  const int split = blockIdx.x % S;
+  const int rest = blockIdx.x / S;
+  const int row = rest % a.Nq;
+  const size_t head = rest / a.Nq;
+  const size_t kvh = kv_head_index((int)(head / a.H), (int)(head % a.H), a.H, a.H_kv);
+  const int kbeg = split_begin(split, a.Nk, S);
+  // Under the causal mask this row sees keys up to row + causal_off; the range may be empty.
+  const int kend = a.causal ? min(split_begin(split + 1, a.Nk, S), row + a.causal_off + 1)
+                            : split_begin(split + 1, a.Nk, S);
+  const float* __restrict__ K = static_cast<const float*>(a.k) + kvh * (size_t)a.Nk * D;
+  const float* __restrict__ V = static_cast<const float*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane / LPK;
+  const int j = lane % LPK;
+  const int nsteps = kend > kbeg ? (kend - kbeg + NW * G - 1) / (NW * G) : 0;
+  // key of this lane's group at step i
+  auto key_at = [&](int i) { return kbeg + (i * NW + wave) * G + grp; };
+
+  float q[CPL], acc[CPL], comp[CPL], tacc[CPL];
+  load_key_cols<D>(static_cast<const float*>(a.q) + (head * a.Nq + row) * (size_t)D, j, q);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = comp[c] = tacc[c] = 0.f;
+  float m = -INFINITY, l = 0.f, lcomp = 0.f, tl = 0.f;
+  auto flush = [&]() {
+    kahan_add(l, lcomp, tl);
+    tl = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      kahan_add(acc[c], comp[c], tacc[c]);
+      tacc[c] = 0.f;
+    }
+  };
+
+  float kb[P][CPL], vb[P][CPL];
+  // rows past kend repeat row kend - 1 (their keys take no part)
+  auto load_step = [&](int i, float (&kx)[CPL], float (&vx)[CPL]) {
+    const size_t key = (size_t)min(key_at(i), kend - 1);
+    load_key_cols<D>(K + key * D, j, kx);
+    load_key_cols<D>(V + key * D, j, vx);
+  };
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < nsteps) load_step(p, kb[p], vb[p]);
+  for (int i0 = 0; i0 < nsteps; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int i = i0 + p;
+      if (i >= nsteps) break;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) dot = __builtin_fmaf(q[c], kb[p][c], dot);
+      dot = group_sum<LPK>(dot);
+      if (key_at(i) < kend) {
+        const float sc = a.scale * dot;
+        if (sc > m) {                        // the max grew: rescale by exp(m_old - m_new)
+          const float alpha = (m == -INFINITY) ? 0.f : expf(m - sc);
+          l *= alpha;
+          lcomp *= alpha;
+          tl *= alpha;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            acc[c] *= alpha;
+            comp[c] *= alpha;
+            tacc[c] *= alpha;
+          }
+          m = sc;
+        }
+        const float pw = expf(sc - m);
+        tl += pw;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) tacc[c] = __builtin_fmaf(pw, vb[p][c], tacc[c]);
+      }
+      if ((i & 7) == 7) flush();
+      if (i + P < nsteps) load_step(i + P, kb[p], vb[p]);
+    }
+  }
+  flush();
+
+  // ---- merge: the G groups of each wave, then the NW waves (all compensated) ----
+  float* st = st_all + wave * WSTATE;
+  if (j == 0) {
+    st[grp] = m;
+    st[G + grp] = l - lcomp;
+  }
+#pragma unroll
+  for (int r = 0; r < CPL / 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st[2 * G + grp * D + r * 4 * LPK + 4 * j + c] = acc[4 * r + c] - comp[4 * r + c];
+  __syncthreads();
+  // each wave folds its own groups: lane -> D / 64 columns
+  constexpr int CW = D / 64;
+  float wm = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) wm = fmaxf(wm, st[g]);
+  float wl = 0.f, wlc = 0.f, wo[CW], woc[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) wo[i] = woc[i] = 0.f;
+  if (wm != -INFINITY) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mg = st[g];
+      if (mg == -INFINITY) continue;         // a group that saw no key weighs 0
+      const float w = expf(mg - wm);
+      kahan_add(wl, wlc, w * st[G + g]);
+#pragma unroll
+      for (int i = 0; i < CW; ++i) kahan_add(wo[i], woc[i], w * st[2 * G + g * D + lane * CW + i]);
+    }
+  }
+  __syncthreads();
+  constexpr int WS2 = 2 + D;
+  static_assert(NW * WS2 <= NW * WSTATE, "wave states do not fit");
+  if (lane == 0) {
+    st_all[wave * WS2] = wm;
+    st_all[wave * WS2 + 1] = wl - wlc;
+  }
+#pragma unroll
+  for (int i = 0; i < CW; ++i) st_all[wave * WS2 + 2 + lane * CW + i] = wo[i] - woc[i];
+  __syncthreads();
+  if (tid >= D) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, st_all[w * WS2]);
+  float L = 0.f, Lc = 0.f, o = 0.f, oc = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = st_all[w * WS2];
+      if (mw == -INFINITY) continue;
+      const float wgt = expf(mw - M);
+      kahan_add(L, Lc, wgt * st_all[w * WS2 + 1]);
+      kahan_add(o, oc, wgt * st_all[w * WS2 + 2 + tid]);
+    }
+  }
+  L -= Lc;
+  o -= oc;
+  const size_t qrow = head * a.Nq + row;
+  if (a.split_mode == 0) {
+    static_cast<float*>(a.o)[qrow * D + tid] = o / L;
+    if (tid == 0) {
+      if (a.m_out) a.m_out[qrow] = M;
+      if (a.l_out) a.l_out[qrow] = L;
+      if (a.lse_out) a.lse_out[qrow] = M + logf(L);
+    }
+  } else {
+    const size_t prow = (size_t)split * a.B * a.H * a.Nq + qrow;
+    // (lse, o / l) form: an empty range keeps (-inf, 0)
+    a.part_o[prow * D + tid] = (a.split_mode == 2) ? (L > 0.f ? o / L : 0.f) : o;
+    if (tid == 0) {
+      if (a.split_mode == 2) {
+        a.part_m[prow] = (M == -INFINITY) ? -INFINITY : M + logf(L);
+      } else {
+        a.part_m[prow] = M;
+        a.part_l[prow] = L;
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   const int n_qtiles = (a.Nq + kRows - 1) / kRows;
@@ -293,6 +511,17 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s) {
   if (d == 64) return launch_typed<64>(a, s);
   if (d == 128) return launch_typed<128>(a, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_f32_rows(const FwdArgs& a, int d, hipStream_t s) {
+  const long long nwg = (long long)a.num_splits * a.Nq * a.H * a.B;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  FwdArgs args = a;
+  void* kargs[] = {&args};
+  const void* k = d == 64 ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<64>)
+                : d == 128 ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<128>) : nullptr;
+  if (!k) return hipErrorInvalidValue;
+  return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreadsRows), kargs, 0, s);
 }
 
 }  // namespace fa

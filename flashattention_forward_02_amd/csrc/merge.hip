@@ -5,8 +5,13 @@
 // (derived from the recurrence of "从零手写 FlashAttention" §4):
 //   m = max(m_a, m_b);  l = l_a e^(m_a - m) + l_b e^(m_b - m);  o = o_a e^(m_a - m) + o_b e^(m_b - m)
 // A state with m = -inf holds no keys and gets weight 0, so -inf - (-inf) is never evaluated.
-// The answer is o / l; a row whose states are all empty (l = 0) gets O = 0, as in the (lse, o) form. One thread handles 4 columns of one row; the partial-state reads are
-// coalesced 16-byte loads.
+// The answer is o / l; a row whose states are all empty (l = 0) gets O = 0, as in the (lse, o) form.
+//
+// Layout: one thread per 4 columns of a row (C4 = d / 4 threads per row, 256 / C4 rows per
+// workgroup). The arithmetic is a sequential fold over the parts, but the loads are not: the
+// workgroup first stages the order and the row's per-part scalars (m and l, or lse) in LDS with
+// one parallel load each, then reads the parts' o vectors 8 at a time, so a row costs about
+// 2 + S / 8 memory round trips instead of one per part and scalar.
 
 #include "fa_internal.h"
 
@@ -17,48 +22,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 __device__ __forceinline__ float weight(float m_part, float m_total) {
   return (m_part == -INFINITY) ? 0.f : expf(m_part - m_total);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int C4 = D / 4;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = idx / C4;
-  const int c = (int)(idx % C4) * 4;
-  if (row >= a.rows) return;
-
-  float m = -INFINITY, l = 0.f;
-  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < a.S; ++k) {
-    const size_t p = (size_t)a.order[k] * a.rows + row;
-    const float ms = a.part_m[p];
-    const float ls = a.part_l[p];
-    const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.part_o + p * D + c);
-    const float mn = fmaxf(m, ms);
-    const float wa = weight(m, mn), wb = weight(ms, mn);
-    l = l * wa + ls * wb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = o[i] * wa + os[i] * wb;
-    m = mn;
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const size_t e = (size_t)row * D + c;
-  if (a.out_dtype == kF32) {
-    f32x4_t x = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.o) + e) = x;
-  } else if (a.out_dtype == kBF16) {
-    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-    bf16x4_t x = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv), (__bf16)(o[3] * inv)};
-    *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(a.o) + e) = x;
-  } else {
-    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
-    f16x4_t x = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv), (_Float16)(o[3] * inv)};
-    *reinterpret_cast<f16x4_t*>(static_cast<_Float16*>(a.o) + e) = x;
-  }
-  if (c == 0) {
-    if (a.m_out) a.m_out[row] = m;
-    if (a.l_out) a.l_out[row] = l;
-  }
 }
 
 // Store 4 consecutive fp32 output values in the output type.
@@ -76,6 +39,94 @@ __device__ __forceinline__ void store_o4(void* o, size_t e, int out_dtype, const
   }
 }
 
+template <int D>
+struct MergeCfg {
+  static constexpr int C4 = D / 4;        // threads per row
+  static constexpr int RPB = 256 / C4;    // rows per workgroup
+  static constexpr int U = 8;             // partial o vectors in flight per thread
+};
+
+// Dynamic LDS of a merge workgroup: order[S], then per row NV * S scalars.
+template <int D>
+inline size_t merge_lds_bytes(int S, int nv) {
+  return ((size_t)S + (size_t)MergeCfg<D>::RPB * nv * S) * sizeof(float);
+}
+
+// Stages order[] and the row's per-part scalars (x0, and x1 when NV = 2), in fold order, in LDS.
+// Returns false for the threads of rows past the end (after the workgroup barrier).
+template <int D, int NV>
+__device__ __forceinline__ bool stage_scalars(const MergeArgs& a, float* sh, long long row, int c4,
+                                              const float* x0, const float* x1, float*& s0, float*& s1) {
+  typedef MergeCfg<D> C;
+  const int S = a.S;
+  int* sh_order = reinterpret_cast<int*>(sh);
+  for (int k = threadIdx.x; k < S; k += 256) sh_order[k] = a.order[k];
+  __syncthreads();
+  const int lr = threadIdx.x / C::C4;
+  s0 = sh + S + (size_t)lr * NV * S;
+  s1 = s0 + S;
+  const bool live = row < a.rows;
+  if (live) {
+#pragma unroll 4
+    for (int k = c4; k < S; k += C::C4) {
+      const size_t p = (size_t)sh_order[k] * a.rows + row;
+      s0[k] = x0[p];
+      if constexpr (NV == 2) s1[k] = x1[p];
+    }
+  }
+  __syncthreads();
+  return live;
+}
+
+// The row's o vectors of parts k0 .. k0 + U - 1 (in fold order; positions past S repeat part S - 1).
+template <int D>
+__device__ __forceinline__ void load_parts(const MergeArgs& a, const int* sh_order, int k0, long long row, int c,
+                                           f32x4_t (&os)[MergeCfg<D>::U]) {
+#pragma unroll
+  for (int u = 0; u < MergeCfg<D>::U; ++u) {
+    const int k = min(k0 + u, a.S - 1);
+    const size_t p = (size_t)sh_order[k] * a.rows + row;
+    os[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + p * D + c);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  typedef MergeCfg<D> C;
+  extern __shared__ float sh[];
+  const int c4 = threadIdx.x % C::C4;
+  const int c = c4 * 4;
+  const long long row = (long long)blockIdx.x * C::RPB + threadIdx.x / C::C4;
+  float *sm, *sl;
+  if (!stage_scalars<D, 2>(a, sh, row, c4, a.part_m, a.part_l, sm, sl)) return;
+  const int* sh_order = reinterpret_cast<const int*>(sh);
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.S; k0 += C::U) {
+    f32x4_t os[C::U];
+    load_parts<D>(a, sh_order, k0, row, c, os);
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      if (k0 + u >= a.S) break;
+      const float ms = sm[k0 + u], ls = sl[k0 + u];
+      const float mn = fmaxf(m, ms);
+      const float wa = weight(m, mn), wb = weight(ms, mn);
+      l = l * wa + ls * wb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = o[i] * wa + os[u][i] * wb;
+      m = mn;
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const f32x4_t x = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  store_o4(a.o, (size_t)row * D + c, a.out_dtype, x);
+  if (c == 0) {
+    if (a.m_out) a.m_out[row] = m;
+    if (a.l_out) a.l_out[row] = l;
+  }
+}
+
 // The (lse, o) form of "CS349E 第 11 讲 01_online_softmax.py" demo 2's note on flash-decoding: each
 // part stores its output already divided by its own l and lse_s = m_s + ln(l_s); the parts are
 // combined with weights exp(lse_s - lse), lse = ln(sum_s exp(lse_s)) (taken as max + ln of the sum
@@ -83,31 +134,39 @@ __device__ __forceinline__ void store_o4(void* o, size_t e, int out_dtype, const
 // empty gets O = 0 and lse = -inf. Sums run in the caller's order.
 template <int D>
 __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
-  constexpr int C4 = D / 4;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = idx / C4;
-  const int c = (int)(idx % C4) * 4;
-  if (row >= a.rows) return;
+  typedef MergeCfg<D> C;
+  extern __shared__ float sh[];
+  const int c4 = threadIdx.x % C::C4;
+  const int c = c4 * 4;
+  const long long row = (long long)blockIdx.x * C::RPB + threadIdx.x / C::C4;
+  float *sl, *unused;
+  if (!stage_scalars<D, 1>(a, sh, row, c4, a.part_m, nullptr, sl, unused)) return;
+  const int* sh_order = reinterpret_cast<const int*>(sh);
+
   float mx = -INFINITY;
-  for (int k = 0; k < a.S; ++k) mx = fmaxf(mx, a.part_m[(size_t)a.order[k] * a.rows + row]);
+  for (int k = 0; k < a.S; ++k) mx = fmaxf(mx, sl[k]);
   float sum = 0.f;
   if (mx != -INFINITY) {
     for (int k = 0; k < a.S; ++k) {
-      const float ls = a.part_m[(size_t)a.order[k] * a.rows + row];
+      const float ls = sl[k];
       if (ls != -INFINITY) sum += expf(ls - mx);
     }
   }
   const float lse = (mx == -INFINITY) ? -INFINITY : mx + logf(sum);
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
-    for (int k = 0; k < a.S; ++k) {
-      const size_t p = (size_t)a.order[k] * a.rows + row;
-      const float ls = a.part_m[p];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - lse);
-      const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.part_o + p * D + c);
+    for (int k0 = 0; k0 < a.S; k0 += C::U) {
+      f32x4_t os[C::U];
+      load_parts<D>(a, sh_order, k0, row, c, os);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(w, os[i], o[i]);
+      for (int u = 0; u < C::U; ++u) {
+        if (k0 + u >= a.S) break;
+        const float ls = sl[k0 + u];
+        if (ls == -INFINITY) continue;
+        const float w = expf(ls - lse);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(w, os[u][i], o[i]);
+      }
     }
   }
   store_o4(a.o, (size_t)row * D + c, a.out_dtype, o);
@@ -116,14 +175,14 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 
 template <int D>
 hipError_t launch_typed(const MergeArgs& a, hipStream_t s) {
-  const long long threads = (long long)a.rows * (D / 4);
-  const long long blocks = (threads + 255) / 256;
+  const long long blocks = ((long long)a.rows + MergeCfg<D>::RPB - 1) / MergeCfg<D>::RPB;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   MergeArgs args = a;
   void* kargs[] = {&args};
   const void* k = a.lse_format ? reinterpret_cast<const void*>(&merge_lse_kernel<D>)
                                : reinterpret_cast<const void*>(&merge_kernel<D>);
-  return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), kargs, 0, s);
+  const size_t lds = merge_lds_bytes<D>(a.S, a.lse_format ? 1 : 2);
+  return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), kargs, lds, s);
 }
 
 }  // namespace
