@@ -352,6 +352,51 @@ def test_merge_of_all_empty_parts_gives_zero(d):
     assert np.max(np.abs(o[0, 0] - ref)) < 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("S,rows", [(9, 17), (200, 37), (256, 5), (1, 3)], ids=str)
+@pytest.mark.parametrize("lse_form", [False, True], ids=["mlo", "lse"])
+def test_merge_many_parts(d, S, rows, lse_form):
+    """Up to FA_MAX_SPLITS parts, a part count that is not a multiple of the 8 read at a time, more parts
+    than threads per row, row counts that leave a workgroup partly empty, and empty parts (m or lse = -inf)
+    scattered in: the merge against the oracle's sequential fold (or its (lse, o) combination) in the
+    same shuffled order."""
+    r = np.random.default_rng(1000 * S + rows + d)
+    order = list(r.permutation(S))
+    empty = r.random((S, rows)) < 0.2
+    empty[order[0], 0] = True                # the first part of the fold is empty for row 0
+    m = (3.0 * r.standard_normal((S, 1, 1, rows))).astype(np.float32)
+    l = (0.5 + r.random((S, 1, 1, rows))).astype(np.float32)
+    o = r.standard_normal((S, 1, 1, rows, d)).astype(np.float32)
+    m[:, 0, 0][empty] = -np.inf
+    l[:, 0, 0][empty] = 0.0
+    o[:, 0, 0][empty] = 0.0
+    say(f"merge many parts d={d} S={S} rows={rows} lse={lse_form}")
+    if lse_form:
+        out, lse = fa.merge_lse(*[torch.from_numpy(x).to(DEV) for x in (m, o)], order=order)
+        torch.cuda.synchronize()
+        ref_lse, ref_o = oracle.merge_lse([(m[c, 0, 0].astype(np.float64), o[c, 0, 0].astype(np.float64))
+                                           for c in range(S)], order=order)
+        got_lse = si.torch_to_f64(lse)[0, 0]
+        live = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(got_lse), live)
+        assert np.max(np.abs(got_lse[live] - ref_lse[live])) < 1e-5
+    else:
+        out, mm, ll = fa.merge_states(*[torch.from_numpy(x).to(DEV) for x in (m, l, o)], order=order,
+                                      return_stats=True)
+        torch.cuda.synchronize()
+        states = [(m[c, 0, 0].astype(np.float64), l[c, 0, 0].astype(np.float64), o[c, 0, 0].astype(np.float64))
+                  for c in range(S)]
+        ref_m, ref_l, ref_acc = oracle.merge_sequential(states, order=order)
+        ref_o = oracle.finish_state((ref_m, ref_l, ref_acc))
+        got_m, got_l = si.torch_to_f64(mm)[0, 0], si.torch_to_f64(ll)[0, 0]
+        live = np.isfinite(ref_m)
+        assert np.array_equal(np.isfinite(got_m), live)
+        assert np.array_equal(got_m[live], ref_m[live].astype(np.float32).astype(np.float64))   # max is exact
+        assert np.max(np.abs(got_l[live] / ref_l[live] - 1)) < 1e-5
+    got_o = si.torch_to_f64(out)[0, 0]
+    assert np.max(np.abs(got_o - ref_o)) < 2e-5
+
+
 def test_decode_bf16_full_size_split16_shuffled_merge():
     """B=16, H=32, one query, Nk=32768, d=128 bf16; 16 splits merged in default_rng(5).permutation(16) order;
     64 whole heads against the oracle."""
