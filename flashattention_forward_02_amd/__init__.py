@@ -264,6 +264,15 @@ def probe_mfma_bf16(nblocks=2048, iters=1024, out=None):
     return float(nblocks) * 4 * iters * 8 * 32768, out
 
 
+def probe_mfma_f32(nblocks=2048, iters=1024, out=None):
+    """Launch the fp32 matrix-core probe of fa_probe.h on the current stream; returns (flops, out)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(nblocks * 256, dtype=torch.float32, device="cuda")
+    _native.check(_native.fa_probe_mfma_f32(out.data_ptr(), out.numel(), nblocks, iters, _stream_ptr(out.device)))
+    return float(nblocks) * 4 * iters * 8 * 2048, out
+
+
 def probe_hbm_read(buf, nblocks=4096, out=None):
     """Launch the streaming-read probe of fa_probe.h over every byte of the device tensor ``buf``; returns the
     number of bytes read. ``out`` (optional) is an int32 device tensor of at least nblocks * 256 elements."""

@@ -15,7 +15,7 @@ FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 256
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_ext", "fa_fwd_split_ext", "fa_fwd_lse", "fa_bwd", "fa_merge_states",
            "fa_fwd_split_lse", "fa_merge_lse", "fa_status_string", "fa_last_error", "fa_abi_version",
-           "fa_probe_mfma_bf16", "fa_probe_hbm_read", "fa_bwd_noalloc")
+           "fa_probe_mfma_bf16", "fa_probe_hbm_read", "fa_bwd_noalloc", "fa_probe_mfma_f32")
 FA_NOALLOC_MAX_ROWS = 4194304
 
 _lib = None
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         LL = ctypes.c_longlong
         L.fa_probe_mfma_bf16.argtypes = [P, LL, I, I, P]
         L.fa_probe_mfma_bf16.restype = I
+        L.fa_probe_mfma_f32.argtypes = [P, LL, I, I, P]
+        L.fa_probe_mfma_f32.restype = I
         L.fa_probe_hbm_read.argtypes = [P, LL, P, LL, I, P]
         L.fa_probe_hbm_read.restype = I
         _lib = L
@@ -141,6 +143,10 @@ def fa_abi_version() -> int:
 
 def fa_probe_mfma_bf16(out, out_elems, nblocks, iters, stream):
     return lib().fa_probe_mfma_bf16(out, out_elems, nblocks, iters, stream)
+
+
+def fa_probe_mfma_f32(out, out_elems, nblocks, iters, stream):
+    return lib().fa_probe_mfma_f32(out, out_elems, nblocks, iters, stream)
 
 
 def fa_probe_hbm_read(src, nbytes, out, out_elems, nblocks, stream):

@@ -445,6 +445,17 @@ fa_status fa_probe_mfma_bf16(float* out, long long out_elems, int nblocks, int i
   return launched(fn, fa::launch_probe_mfma(out, nblocks, iters, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_probe_mfma_f32(float* out, long long out_elems, int nblocks, int iters, void* stream) {
+  g_last_error[0] = 0;
+  const char* fn = "fa_probe_mfma_f32";
+  if (nblocks < 1 || nblocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return fail(FA_EINVAL, "%s: nblocks=%d and iters=%d must be in [1, 2^20]", fn, nblocks, iters);
+  if (!out || !aligned4(out) || out_elems < (long long)nblocks * 256)
+    return fail(FA_EINVAL, "%s: out must be a 4-byte aligned device buffer of >= nblocks * 256 = %lld floats", fn,
+                (long long)nblocks * 256);
+  return launched(fn, fa::launch_probe_mfma_f32(out, nblocks, iters, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_probe_hbm_read(const void* src, long long bytes, unsigned* out, long long out_elems, int nblocks,
                             void* stream) {
   g_last_error[0] = 0;

@@ -93,6 +93,7 @@ hipError_t launch_fwd_f32_rows(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, int d, int in_dtype, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int d, hipStream_t s);
 hipError_t launch_probe_mfma(float* out, int nblocks, int iters, hipStream_t s);
+hipError_t launch_probe_mfma_f32(float* out, int nblocks, int iters, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, unsigned* out, int nblocks, hipStream_t s);
 
 // Query-row count up to which the split/decode kernel (one workgroup per query row and key

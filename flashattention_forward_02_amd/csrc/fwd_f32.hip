@@ -1,6 +1,10 @@
-// Tiled FlashAttention forward for fp32 inputs (VALU, full fp32 arithmetic).
+// FlashAttention forward for fp32 inputs: three kernels.
+//  * fwd_f32_kernel (this header): more than 16 query rows at d = 128, on the VALU.
+//  * fwd_f32_mfma_kernel: more than 16 query rows at d = 64, the products on the fp32 matrix
+//    cores (described above it).
+//  * fwd_f32_rows_kernel: up to 16 query rows, keys spread over the lanes (described above it).
 //
-// Same recurrence as the matrix-core kernel ("FlashAttention 简化版：Tiling + Online Softmax",
+// fwd_f32_kernel. Same recurrence as the matrix-core kernel ("FlashAttention 简化版：Tiling + Online Softmax",
 // §2.3 and §3.1), written for accuracy: scores are s = scale * (q . k) in fp32, the running max
 // is taken on s, and exp is the accurate expf, so the result tracks the float64 definition to a
 // few fp32 ulps.
@@ -23,9 +27,6 @@
 // would lose ~sqrt(Nk) ulps. Each tile's contribution (16 or 8 keys) is summed plainly and then
 // added to the running l and accumulator with compensation (Kahan), and the merge of the 8 wave
 // states is compensated too: the error grows with the tile length, not with Nk.
-//
-// Up to 16 query rows go to fwd_f32_rows_kernel instead (one workgroup per key range, row and
-// head, keys spread over the lanes; described above the kernel).
 
 #include "fa_internal.h"
 #include "mfma_common.h"
@@ -278,6 +279,317 @@ __global__ __launch_bounds__(kThreadsF) void fwd_f32_kernel(FwdArgs a, int n_qti
   }
 }
 
+// ---- d = 64 on the fp32 matrix cores ----
+// The same decomposition as fwd_f32_kernel (a workgroup owns 16 query rows of one head; each of
+// its NW waves streams its own share of the key range and keeps its own online-softmax state; the
+// NW states are merged with compensation at the end), with the two products on
+// v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation, at twice the rate of plain fp32 FMAs
+// on the VALU, which is left with the softmax.
+//  * S^T = K Q^T per 16-key step: rows = keys, columns = the 16 queries. In the 16x16 result a
+//    lane owns one query (lane % 16) and 4 consecutive keys (4 (lane / 16) + r), so the row max
+//    and sum need two exchanges (lanes 16 and 32 apart). The 64 dimensions are taken in the order
+//    that lets one 16-byte load feed four k-steps: k-step (G, i) gives group g = lane / 16 the
+//    dimension 16 G + 4 g + i (Q^T, in registers, follows the same order).
+//  * O^T += V^T P^T: the B operand of k-step kk is P at key 4 g + kk, the lane's own score
+//    register kk, so P never leaves the lane. Row m of output block db is dimension 4 m + db, so
+//    the A operands a lane feeds the 4 blocks at one key are 4 consecutive floats of one V row:
+//    one 16-byte load per key.
+//  * K and V go straight from memory into registers in exactly those operand layouts (a step is
+//    8 16-byte buffer loads per lane, addressed by a scalar descriptor and immediates); no LDS
+//    until the merge. The scores of step t + 1 are issued before the softmax of step t.
+//  * Exponentials in base 2, as in the matrix-core kernel: with c = scale * log2(e), p =
+//    2^(s c - m2) is one FMA and one v_exp_f32, against about 13 instructions for expf. VALU
+//    instructions do not overlap the fp32 MFMAs of the same SIMD (a probe: 16 MFMAs take 512
+//    cycles, and each VALU instruction beside them adds about 7), so the VALU count sets the
+//    rate; the rounding of the argument s c - m2, which both forms share, dominates the error.
+//    m_out is scale times the running max of the raw dot products, and m2 = that max times c.
+//  * Accuracy as in fwd_f32_kernel otherwise: the PV products of 8 steps (128 keys) accumulate
+//    plainly in the matrix core and are then added with compensation, as is l; the merge of the
+//    wave states is compensated.
+constexpr int kQM = 16;                     // query rows per workgroup
+constexpr int kKM = 16;                     // keys per step
+// Fourth word of a raw buffer descriptor (32-bit data format, no swizzle, no stride).
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Max / sum over the 4 lanes that hold one query (lanes 16 apart).
+__device__ __forceinline__ float qrow_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float qrow_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_f32_mfma_kernel(FwdArgs a, int n_qtiles) {
+  constexpr int D = 64;
+  // merge state per wave: m2[16], l[16], mraw[16], then O[16][64] (compensated values)
+  constexpr int WST = 3 * kQM + kQM * D;
+  __shared__ float st_all[NW * WST];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = wg % n_qtiles;
+  int rest = wg / n_qtiles;
+  const int split = rest % a.num_splits;
+  rest /= a.num_splits;
+  const int h = rest % a.H;
+  const int b = rest / a.H;
+  const size_t head = (size_t)b * a.H + h;
+  const size_t kvh = kv_head_index(b, h, a.H, a.H_kv);
+  const float* __restrict__ Q = static_cast<const float*>(a.q) + head * (size_t)a.Nq * D;
+  const float* __restrict__ K = static_cast<const float*>(a.k) + kvh * (size_t)a.Nk * D;
+  const float* __restrict__ V = static_cast<const float*>(a.v) + kvh * (size_t)a.Nk * D;
+  const int kbeg = split_begin(split, a.Nk, a.num_splits);
+  int kend = split_begin(split + 1, a.Nk, a.num_splits);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;     // this lane's query (MFMA column) and the K row it supplies
+  const int g = lane >> 4;     // its k-index group
+  const int row = qt * kQM + n;
+  const bool live = row < a.Nq;
+  // Causal mask: this row sees keys < row_end; every row of the workgroup sees the keys below
+  // all_end; the workgroup's range ends after the last key its last row sees.
+  int row_end = kend, all_end = kend;
+  if (a.causal) {
+    row_end = min(kend, row + a.causal_off + 1);
+    all_end = min(kend, qt * kQM + a.causal_off + 1);
+    kend = min(kend, min(a.Nq, (qt + 1) * kQM) + a.causal_off);
+  }
+  const int nsteps = kend > kbeg ? (kend - kbeg + kKM - 1) / kKM : 0;
+  const int t0 = (int)(((long long)wave * nsteps) / NW);
+  const int t1 = (int)(((long long)(wave + 1) * nsteps) / NW);
+
+  // Q^T operand: qv[4 G + i] = Q[row][16 G + 4 g + i]
+  float qv[16];
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+    if (live) x = *reinterpret_cast<const f32x4_t*>(Q + (size_t)row * D + 16 * G + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qv[4 * G + i] = x[i];
+  }
+  // Operands of one step, per lane: kx[4 G + i] = K[key0 + n][16 G + 4 g + i] (S^T A operands),
+  // vx[4 kk + db] = V[key0 + 4 g + kk][4 n + db] (O^T A operands). Byte offsets from the step's
+  // first key row: K n * 256 + g * 16 (+ 64 G), V 4 g * 256 + n * 16 (+ 256 kk).
+  const unsigned koffb = (unsigned)(n * 256 + g * 16);
+  const unsigned voffb = (unsigned)(g * 1024 + n * 16);
+  // Buffer loads: the descriptor of a step starts at its first key row and holds the rows up to
+  // kend, so the rows of a ragged last step that lie past kend read as 0 (the hardware's range
+  // check; their scores are masked) and no load branches. Steps past the wave's last one are
+  // clamped to it (those loads are not used).
+  auto step_rsrc = [&](const float* X, int t) {
+    const int key0 = kbeg + min(t, t1 - 1) * kKM;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(X + (size_t)key0 * D), 0,
+                                             (kend - key0) * D * (int)sizeof(float), kBufferWord3);
+  };
+  auto load_k = [&](int t, float (&kx)[16]) {
+    const __amdgpu_buffer_rsrc_t r = step_rsrc(K, t);
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, koffb + 64 * G, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kx[4 * G + i] = x[i];
+    }
+  };
+  auto load_v = [&](int t, float (&vx)[16]) {
+    const __amdgpu_buffer_rsrc_t r = step_rsrc(V, t);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voffb + 256 * kk, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vx[4 * kk + i] = x[i];
+    }
+  };
+
+  // per lane: the query's running max of the raw dot products (shared by its 4 lanes) and its
+  // base-2 exponent reference m2 = mraw * c, this lane's share of l = sum 2^(s c - m2), and
+  // O^T[16 g + 4 r + db][query] in acc[db][r]; bl / bacc are the plain sums of the current 8 steps
+  const float c = a.scale_log2e;
+  float mraw = -INFINITY, m2 = -INFINITY, l = 0.f, lcomp = 0.f, bl = 0.f;
+  float acc[4][4], comp[4][4];
+  f32x4_t bacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[db][i] = comp[db][i] = bacc[db][i] = 0.f;
+  auto flush = [&]() {
+    kahan_add(l, lcomp, bl);
+    bl = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kahan_add(acc[db][i], comp[db][i], (float)bacc[db][i]);
+        bacc[db][i] = 0.f;
+      }
+  };
+
+  auto scores = [&](const float (&kx)[16]) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s = mfma_f32(kx[k], qv[k], s);
+    return s;
+  };
+  // softmax update and O^T += V^T P^T of step t, given its raw scores
+  auto update = [&](int t, const f32x4_t& s, const float (&vx)[16]) {
+    const int key0 = kbeg + t * kKM;
+    const bool full = key0 + kKM <= all_end;   // every key of the step is seen by every row
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (full || key0 + 4 * g + r < row_end) mt = fmaxf(mt, s[r]);
+    mt = qrow_max(mt);
+    const bool grow = mt > mraw;             // false while the query has seen no key (both -inf)
+    if (__ballot(grow)) {                    // rescale l and the accumulators by 2^(m2_old - m2_new)
+      const float m2new = grow ? mt * c : m2;
+      const float alpha = grow ? (mraw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - m2new)) : 1.f;
+      l *= alpha;
+      lcomp *= alpha;
+      bl *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[db][i] *= alpha;
+          comp[db][i] *= alpha;
+          bacc[db][i] *= alpha;
+        }
+      if (grow) {
+        mraw = mt;
+        m2 = m2new;
+      }
+    }
+    float p[4];
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m2));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p[r] = (key0 + 4 * g + r < row_end) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m2)) : 0.f;
+    }
+    bl += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) bacc[db] = mfma_f32(vx[4 * kk + db], p[kk], bacc[db]);
+    if (((t - t0) & 7) == 7) flush();
+  };
+
+  // Software pipeline: iteration t issues the scores of step t + 1 (matrix cores) before the
+  // softmax of step t (VALU), so a wave's own MFMAs run under its softmax. K is loaded two steps
+  // ahead of its use (one step ahead of its scores), V one step ahead; the loop is unrolled by two
+  // so the buffers are fixed registers: at the top of iteration t, K(t + 1) is in kb1, V(t) in vb0
+  // and the scores of step t in s_cur.
+  float kb0[16], vb0[16], kb1[16], vb1[16];
+  if (t0 < t1) {
+    load_k(t0, kb0);
+    load_v(t0, vb0);
+    load_k(t0 + 1, kb1);
+    f32x4_t s_cur = scores(kb0);
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
+      load_k(t + 2, kb0);
+      load_v(t + 1, vb1);
+      const f32x4_t s_nxt = scores(kb1);
+      update(t, s_cur, vb0);
+      load_k(t + 3, kb1);
+      load_v(t + 2, vb0);
+      s_cur = scores(kb0);
+      update(t + 1, s_nxt, vb1);
+    }
+    if (t < t1) update(t, s_cur, vb0);
+  }
+  flush();
+
+  // ---- merge the NW wave states of every row (compensated), then the epilogue ----
+  {
+    float* st = st_all + wave * WST;
+    const float lq = qrow_sum(l - lcomp);
+    if (g == 0) {
+      st[n] = m2;
+      st[kQM + n] = lq;
+      st[2 * kQM + n] = mraw;
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[3 * kQM + n * D + 16 * g + 4 * r + db] = acc[db][r] - comp[db][r];
+  }
+  __syncthreads();
+
+  // thread -> (row r, 2 consecutive columns): 16 rows x 64 columns over the first 512 threads
+  constexpr int CPT = 2;
+  static_assert(NW * 64 >= kQM * D / CPT, "every output column needs a thread");
+  if (tid >= kQM * D / CPT) return;
+  const int r = tid / (D / CPT);
+  const int cc = (tid % (D / CPT)) * CPT;
+  const int grow_ = qt * kQM + r;
+  float M2 = -INFINITY, MR = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    M2 = fmaxf(M2, st_all[w * WST + r]);
+    MR = fmaxf(MR, st_all[w * WST + 2 * kQM + r]);
+  }
+  float L = 0.f, Lc = 0.f, o[CPT], oc[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) o[i] = oc[i] = 0.f;
+  if (M2 != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* ws = st_all + w * WST;
+      const float mw = ws[r];
+      if (mw == -INFINITY) continue;      // a wave that saw no key of this row weighs 0
+      const float wgt = __builtin_amdgcn_exp2f(mw - M2);
+      kahan_add(L, Lc, wgt * ws[kQM + r]);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) kahan_add(o[i], oc[i], wgt * ws[3 * kQM + r * D + cc + i]);
+    }
+  }
+  L -= Lc;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) o[i] -= oc[i];
+  if (grow_ >= a.Nq) return;
+  // m = scale * max of the raw dot products; L = sum 2^(s c - M2) with M2 = max * c (the same
+  // rounded product every wave used), i.e. l relative to m; lse = M2 ln 2 + ln L
+  const float M = a.scale * MR;
+  const float lse = M2 * 0.6931471805599453f + logf(L);
+
+  if (a.split_mode == 0) {
+    const float inv = 1.f / L;
+    float* O = static_cast<float*>(a.o) + (head * (size_t)a.Nq + grow_) * D + cc;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) O[i] = o[i] * inv;
+    if (cc == 0) {
+      if (a.m_out) a.m_out[head * a.Nq + grow_] = M;
+      if (a.l_out) a.l_out[head * a.Nq + grow_] = L;
+      if (a.lse_out) a.lse_out[head * a.Nq + grow_] = lse;
+    }
+  } else {
+    const size_t prow = ((size_t)split * a.B * a.H + head) * a.Nq + grow_;
+    float* P = a.part_o + prow * D + cc;
+    // (lse, o / l) form: a row with no key in this range keeps (-inf, 0)
+    const float w = (a.split_mode == 2) ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) P[i] = o[i] * w;
+    if (cc == 0) {
+      if (a.split_mode == 2) {
+        a.part_m[prow] = (M2 == -INFINITY) ? -INFINITY : lse;
+      } else {
+        a.part_m[prow] = (M2 == -INFINITY) ? -INFINITY : M;
+        a.part_l[prow] = L;
+      }
+    }
+  }
+}
+
 // ---- few query rows (Nq <= 16): one workgroup per (key range, row, head), keys across lanes ----
 // With one row per workgroup there is nothing to share through LDS, and the time goes to memory
 // round trips, not arithmetic. So the roles of rows and keys swap inside a wave: the wave holds
@@ -507,8 +819,21 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_fwd_f32_mfma(const FwdArgs& a, hipStream_t s) {
+  // 8 waves (two per SIMD): 12 measured no faster, 16 slower (their registers spill)
+  constexpr int NW = 8;
+  const int n_qtiles = (a.Nq + kQM - 1) / kQM;
+  const long long nwg = (long long)n_qtiles * a.num_splits * a.H * a.B;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  FwdArgs args = a;
+  int nq = n_qtiles;
+  void* kargs[] = {&args, &nq};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f32_mfma_kernel<NW>), dim3((unsigned)nwg), dim3(NW * 64),
+                         kargs, 0, s);
+}
+
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s) {
-  if (d == 64) return launch_typed<64>(a, s);
+  if (d == 64) return launch_fwd_f32_mfma(a, s);
   if (d == 128) return launch_typed<128>(a, s);
   return hipErrorInvalidValue;
 }

@@ -3,6 +3,7 @@
 //  * probe_mfma_kernel: back-to-back 32x32x16 bf16 MFMAs on register operands, eight independent
 //    accumulators per wave so the matrix core never waits on a result. Its rate is the
 //    matrix-core throughput this chip sustains at the clock it runs at under that load.
+//  * probe_mfma_f32_kernel: the same with 16x16x4 fp32 MFMAs (the fp32 matrix-core rate).
 //  * probe_read_kernel: a streaming 16-byte-per-lane read of a large buffer (each byte once), the
 //    HBM read bandwidth a memory-bound kernel can reach.
 //
@@ -45,6 +46,23 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(float* __rest
   out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
 }
 
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma_f32_kernel(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  // small operands (|x| <= 2^-7): the accumulators stay finite for any iteration count used here
+  const float a = (float)(lane & 15) * (1.f / 2048.f), b = (float)(lane >> 4) * (1.f / 1024.f);
+  f32x4_t acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) s += (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]);
+  out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ src, size_t n16,
                                                                     unsigned* __restrict__ out) {
   const size_t stride = (size_t)gridDim.x * kProbeThreads;
@@ -70,6 +88,11 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
 
 hipError_t launch_probe_mfma(float* out, int nblocks, int iters, hipStream_t s) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)nblocks), dim3(kProbeThreads), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_f32(float* out, int nblocks, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(probe_mfma_f32_kernel, dim3((unsigned)nblocks), dim3(kProbeThreads), 0, s, out, iters);
   return hipGetLastError();
 }
 

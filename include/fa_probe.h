@@ -28,6 +28,13 @@ extern "C" {
 fa_status fa_probe_mfma_bf16(float* out, long long out_elems, int nblocks, int iters, void* stream);
 
 /*
+ * fa_probe_mfma_f32 -- the same probe with fp32 MFMAs of shape 16x16x4 (2048 flops each): every
+ * wave issues iters * 8 of them on register operands, eight independent accumulators. Total
+ * work: nblocks * 4 * iters * 8 * 2048 flops. Arguments and errors as fa_probe_mfma_bf16.
+ */
+fa_status fa_probe_mfma_f32(float* out, long long out_elems, int nblocks, int iters, void* stream);
+
+/*
  * fa_probe_hbm_read -- a streaming-read bandwidth probe.
  *
  * Reads every byte of `src` once with 16-byte loads spread over `nblocks` workgroups of 256

@@ -325,11 +325,12 @@ def test_fa_merge_lse_rejects_output_overlapping_states():
     (dict(nblocks=0), "nblocks"), (dict(iters=0), "iters"), (dict(nblocks=(1 << 20) + 1), "nblocks"),
     (dict(out=None), "out"), (dict(out_elems=255), "out"), (dict(out=P + 2), "out"),
 ])
-def test_probe_mfma_rejects(kw, msg):
+@pytest.mark.parametrize("name", ["fa_probe_mfma_bf16", "fa_probe_mfma_f32"])
+def test_probe_mfma_rejects(name, kw, msg):
     a = dict(out=P, out_elems=256, nblocks=1, iters=4, stream=None)
     a.update(kw)
-    assert n.fa_probe_mfma_bf16(**a) == n.FA_EINVAL
-    assert msg in n.fa_last_error()
+    assert getattr(n, name)(**a) == n.FA_EINVAL
+    assert msg in n.fa_last_error() and name in n.fa_last_error()
 
 
 @pytest.mark.parametrize("kw,msg", [

@@ -1,8 +1,9 @@
 """The measurement probes of include/fa_probe.h on the GPU (through the C ABI via the package binding).
 
 The streaming-read probe must read every 16-byte chunk of its buffer exactly once: its per-thread XOR
-checksums are recomputed on the host from the grid-stride assignment. The matrix-core probe must
-produce finite checksums that are identical in every workgroup (each computes the same products).
+checksums are recomputed on the host from the grid-stride assignment. The matrix-core probes (bf16 and
+fp32) must produce finite checksums that are identical in every workgroup (each computes the same
+products); the fp32 one is also compared with its closed form.
 """
 import numpy as np
 import pytest
@@ -41,3 +42,20 @@ def test_mfma_probe_is_deterministic_and_finite():
     x = out.view(32, 256).cpu().numpy()
     assert np.all(np.isfinite(x)) and np.any(x != 0)
     assert np.array_equal(x, np.broadcast_to(x[0], x.shape))
+
+
+def test_mfma_f32_probe_is_deterministic_and_matches_its_closed_form():
+    nblocks, iters = 16, 40
+    flops, out = fa.probe_mfma_f32(nblocks=nblocks, iters=iters)
+    torch.cuda.synchronize()
+    assert flops == nblocks * 4 * iters * 8 * 2048
+    x = out.view(nblocks, 256).cpu().numpy()
+    assert np.array_equal(x, np.broadcast_to(x[0], x.shape))
+    # every accumulator element (i, j) of a 16x16x4 chain gains sum_k A[i][k] B[k][j] per MFMA, with lane
+    # l holding A[l % 16][l / 16] = (l % 16) / 2048 and B[l / 16][l % 16] = (l / 16) / 1024; lane l's
+    # four results are rows 4 (l / 16) + r of column l % 16, summed over the 8 chains
+    A = np.array([[(i % 16) / 2048.0 for k in range(4)] for i in range(16)])
+    Bm = np.array([[k / 1024.0 for j in range(16)] for k in range(4)])
+    C = A @ Bm * iters
+    want = np.array([8 * sum(C[4 * (l // 16) + r, l % 16] for r in range(4)) for l in range(64)])
+    assert np.allclose(x[0].reshape(4, 64)[0], want, rtol=1e-5)
