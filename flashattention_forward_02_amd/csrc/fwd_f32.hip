@@ -833,7 +833,8 @@ hipError_t launch_fwd_f32_mfma(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s) {
-  if (d == 64) return launch_fwd_f32_mfma(a, s);
+  // the matrix-core kernel's buffer descriptors count a key range in bytes in 32 bits
+  if (d == 64 && (long long)a.Nk * 64 * (long long)sizeof(float) <= 0x7fffffffLL) return launch_fwd_f32_mfma(a, s);
   if (d == 128) return launch_typed<128>(a, s);
   return hipErrorInvalidValue;
 }
