@@ -503,7 +503,7 @@ def main():
                        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.Nq, "d": wl.d,
                                   "causal": wl.causal, "grad_dtype": "fp32"}})
         achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-        kname = "fa_bwd (bwd_dq_pp + bwd_dkdv_pp)" if wl.d == 64 else "fa_bwd (bwd_delta + bwd_dq + bwd_dkdv)"
+        kname = "fa_bwd (bwd_dq_pp + bwd_dkdv_pp)" if wl.d == 64 else "fa_bwd (bwd_delta + bwd_dq + bwd_dkdv16)"
         result["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, **launch_stats,
                               "traffic": traffic_for(wname, device_code_hash("bwd.hip"))}

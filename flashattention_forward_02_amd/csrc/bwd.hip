@@ -17,10 +17,15 @@
 //    K and V past them in 64-key tiles, exactly like the forward kernel: S^T = K Q^T and
 //    dP^T = V dO^T on 32x32x16 MFMAs with Q and dO held as B operands in registers, then in
 //    registers P^T and dS^T, and dQ^T += K^T dS^T with K^T read from LDS by transposing reads.
-//  * bwd_dkdv: a workgroup owns 128 keys of one (b, h_kv) (32 per wave) and streams the query
-//    rows of every query head of the group past them in 64-row tiles: S = Q K^T and dP = dO V^T
-//    with K and V held as B operands, P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS
-//    with dO^T and Q^T read by transposing reads.
+//  * dK, dV: a workgroup owns keys of one (b, h_kv) and streams the query rows of every query
+//    head of the group past them in 64-row tiles: S = Q K^T and dP = dO V^T with K and V held as
+//    B operands, P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T as
+//    A operands. Under the causal mask earlier key tiles are seen by more query rows, so the key
+//    tile varies slowest in block order, heaviest (first) first; without it the XCD remap keeps a
+//    head's tiles on one L2. The row values are prepared in LDS once per tile by the waves that
+//    load them (after the load lands, before the barrier that publishes the tile): lse scaled by
+//    log2(e), so P = 2^(s c - L log2 e) takes one FMA per element, and +inf for rows past Nq, so
+//    their P is 0 without a mask; D negated, as the initial value of the dP accumulator.
 //  In both, the 32x32 accumulator of S (or S^T) splits into 8-value halves that are the B
 //  operands of the next 16-step MFMAs under the same fixed row permutation the forward kernel
 //  uses for P; the transposing reads follow it. P and dS are rounded to the input type (round to
@@ -30,8 +35,9 @@
 //  free of bank conflicts.
 //  At d = 64 both gradient kernels run as ping-pong kernels (bwd_dq_pp, bwd_dkdv_pp): 8 waves
 //  in two groups in opposite matrix-core / softmax phases, as in the forward kernel, 256 rows
-//  (keys) per workgroup, three rotating tile buffers. The 4-wave kernels above serve d = 128,
-//  whose accumulators do not fit two waves per SIMD.
+//  (keys) per workgroup, three rotating tile buffers. At d = 128 the dQ kernel is the 4-wave one
+//  (two workgroups per compute unit) and dK, dV come from bwd_dkdv16 (16 keys per wave on
+//  16x16x32 MFMAs, so that two waves fit a SIMD; ping-pong as at d = 64).
 
 #include "fa_internal.h"
 #include "mfma_common.h"
@@ -326,195 +332,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a, int n
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: 128 keys of one (b, h_kv) per workgroup, query rows of the group streamed in 64-row tiles
-// ---------------------------------------------------------------------------------------------
-template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
-  typedef BCfg<D, T> C;
-  typedef typename C::v8 v8;
-  // Separate buffers per tensor and parity (see bwd_dq_kernel).
-  __shared__ __attribute__((aligned(16))) T lds_q0[C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_q1[C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_do0[C::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_do1[C::ELEMS];
-  __shared__ __attribute__((aligned(16))) float lds_l0[kTile];
-  __shared__ __attribute__((aligned(16))) float lds_l1[kTile];
-  __shared__ __attribute__((aligned(16))) float lds_d0[kTile];
-  __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
-
-  // Under the causal mask earlier key tiles are seen by more query rows: the key tile varies
-  // slowest in block order, heaviest (first) first.
-  int kt, rest;
-  if constexpr (CAUSAL) {
-    const int units = gridDim.x / n_ktiles;
-    kt = (int)blockIdx.x / units;
-    rest = (int)blockIdx.x % units;
-  } else {
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    kt = wg % n_ktiles;
-    rest = wg / n_ktiles;
-  }
-  const int hk = rest % a.H_kv;
-  const int b = rest / a.H_kv;
-  const int group = a.H / a.H_kv;
-  const size_t kvh = (size_t)b * a.H_kv + hk;
-  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
-  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;
-  const int key = kt * kOwn + wave * 32 + l32;   // this lane's key (column of S)
-  const int keyc = min(key, a.Nk - 1);
-
-  v8 kf[C::KS], vf[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)keyc * D + ks * 16 + hf * 8);
-    vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)keyc * D + ks * 16 + hf * 8);
-  }
-  const float c2 = a.scale_log2e;
-
-  f32x16_t dk[C::DB], dv[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
-
-  // Query tiles: those holding a row that sees the workgroup's first key (all of them unmasked).
-  const int n_rtiles = (a.Nq + kTile - 1) / kTile;
-  int r_begin = 0;
-  if constexpr (CAUSAL) r_begin = max(0, kt * kOwn - a.causal_off) / kTile;
-  const int per_head = n_rtiles - r_begin;
-  const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
-
-  // The row values are prepared in LDS once per tile by the waves that load them (after the load
-  // lands, before the barrier that publishes the tile): lse scaled by log2(e), so P = 2^(s c -
-  // L log2 e) takes one FMA per element, and +inf for rows past Nq, so their P is 0 without a
-  // mask; D negated, as the initial value of the dP accumulator (dP - D comes out of the MFMAs).
-  auto prep_rows = [&](float* ll, float* ld, int r0) __attribute__((always_inline)) {
-    if (wave == 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      ll[lane] = r0 + lane < a.Nq ? ll[lane] * kLog2e : INFINITY;
-    }
-    if (wave == 1) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      ld[lane] = -ld[lane];
-    }
-  };
-  auto issue = [&](int step, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
-    const int h = hk * group + step / per_head;
-    const int r0 = (r_begin + step % per_head) * kTile;
-    const size_t head = (size_t)b * a.H + h;
-    load_tile<D, T>(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lq, r0, a.Nq, wave, lane);
-    load_tile<D, T>(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, ldo, r0, a.Nq, wave, lane);
-    if (wave == 0) load_rowvec(a.lse + head * a.Nq, ll, r0, a.Nq, lane);
-    if (wave == 1) load_rowvec(a.delta + head * a.Nq, ld, r0, a.Nq, lane);
-  };
-
-  if (n_steps > 0) {
-    issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
-    prep_rows(lds_l0, lds_d0, r_begin * kTile);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // One (query head, row tile) step: prefetch the next into the other buffers, compute, wait, barrier.
-  LdsOff<D, T> lo0(lane);
-  auto step = [&](int st, const T* lq, const T* ldo, const float* ll, const float* ld, T* nq, T* ndo, float* nl,
-                  float* nd) __attribute__((always_inline)) {
-    LdsOff<D, T> lo = lo0;
-    lo.opaque();
-    if (st + 1 < n_steps) issue(st + 1, nq, ndo, nl, nd);
-    const int r0 = (r_begin + st % per_head) * kTile;
-    // S = Q K^T and dP - D = dO V^T - D: rows = the tile's 64 query rows (two 32-blocks),
-    // columns = keys. Register r of lane half hf is row 32 qb + acc_row(r, hf): registers
-    // 4 g4 .. 4 g4 + 3 are four consecutive rows, one 16-byte read of -D.
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4_t nD = *reinterpret_cast<const f32x4_t*>(&ld[qb * 32 + 8 * g4 + 4 * hf]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s[qb][4 * g4 + u] = 0.f;
-          dp[qb][4 * g4 + u] = nD[u];
-        }
-      }
-    __builtin_amdgcn_s_setprio(1);   // as in bwd_dq_kernel
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = Mma<T>::mma(row_frag_o<D, T>(lq, lo, qb, ks), kf[ks], s[qb]);
-        dp[qb] = Mma<T>::mma(row_frag_o<D, T>(ldo, lo, qb, ks), vf[ks], dp[qb]);
-      }
-    __builtin_amdgcn_s_setprio(0);
-    // per 16-row step g: P = exp(S - L) (0 for rows past Nq, whose L is +inf, and for masked
-    // keys), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS. Under the causal mask,
-    // register r of lane half hf holds row r0 + 32 qb + acc_row(r, hf), which sees this lane's key
-    // when 32 qb + 8 (r / 4) + r % 4 >= key - causal_off - r0 - 4 hf (= lim).
-    int lim = 0;
-    if constexpr (CAUSAL) lim = key - a.causal_off - r0 - 4 * hf;
-    {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qb = g >> 1;
-        float p[8], ds[8];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int g4 = 2 * (g & 1) + h2;
-          const int i0 = qb * 32 + 8 * g4 + 4 * hf;   // first of the 4 consecutive rows of registers 4 g4 ..
-          const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(&ll[i0]);   // lse * log2(e)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * g4 + u;
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u]));
-            if constexpr (CAUSAL) {
-              if (32 * qb + 8 * g4 + u < lim) x = 0.f;
-            }
-            p[4 * h2 + u] = x;
-            ds[4 * h2 + u] = x * dp[qb][r];
-          }
-        }
-        const v8 pf = pack8<T>(p);
-        const v8 dsf = pack8<T>(ds);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dv[db] = Mma<T>::mma(tr_frag_o<D, T>(ldo, lo, g, db), pf, dv[db]);
-          dk[db] = Mma<T>::mma(tr_frag_o<D, T>(lq, lo, g, db), dsf, dk[db]);
-        }
-      }
-    }
-    if (st + 1 < n_steps) prep_rows(nl, nd, (r_begin + (st + 1) % per_head) * kTile);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-  for (int st = 0; st < n_steps; st += 2) {
-    step(st, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
-    if (st + 1 < n_steps) step(st + 1, lds_q1, lds_do1, lds_l1, lds_d1, lds_q0, lds_do0, lds_l0, lds_d0);
-  }
-
-  if (key < a.Nk) {
-    float* outk = a.dk + (kvh * (size_t)a.Nk + key) * D;
-    float* outv = a.dv + (kvh * (size_t)a.Nk + key) * D;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dd = db * 32 + 8 * g4 + 4 * hf;
-        f32x4_t xk = {a.scale * dk[db][4 * g4], a.scale * dk[db][4 * g4 + 1], a.scale * dk[db][4 * g4 + 2],
-                      a.scale * dk[db][4 * g4 + 3]};
-        f32x4_t xv = {dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]};
-        *reinterpret_cast<f32x4_t*>(outk + dd) = xk;
-        *reinterpret_cast<f32x4_t*>(outv + dd) = xv;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 // dK, dV at d = 64, ping-pong: 8 waves in two groups (A = waves 0-3, B = 4-7; waves w and w + 4
 // share a SIMD) in opposite phases, as in the forward kernel, so one wave of each SIMD keeps the
 // matrix core busy while the other computes P and dS. A workgroup owns 256 keys of one
@@ -570,7 +387,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
   __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
   __shared__ __attribute__((aligned(16))) float lds_d2[kTile];
 
-  // work order as in bwd_dkdv_kernel
+  // work order: see the file header (dK, dV)
   int kt, rest;
   if constexpr (CAUSAL) {
     const int units = gridDim.x / n_ktiles;
@@ -702,8 +519,8 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
   };
 
   auto phase_valu = [&](int t, const float* lc, float* ln, float* dn) __attribute__((always_inline)) {
-    // P = exp(S - L) (0 past Nq through L = +inf; masked keys), dS = P (dP - D), as in
-    // bwd_dkdv_kernel (register r of lane half hf is row 32 qb + acc_row(r, hf))
+    // P = exp(S - L) (0 past Nq through L = +inf; masked keys), dS = P (dP - D); register r of
+    // lane half hf is row 32 qb + acc_row(r, hf)
     const int r0 = row0(t);
     int lim = 0;
     if constexpr (CAUSAL) lim = key - a.causal_off - r0 - 4 * hf;
@@ -1037,6 +854,318 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dq_pp_kernel(BwdArgs a, 
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dK, dV at d = 128, ping-pong with 16 keys per wave. With 32 keys per wave the dK, dV
+// accumulators and the K, V operands alone take 256 registers, so each SIMD runs one wave
+// and its matrix core waits whenever that wave computes P and dS. Here a wave owns 16 keys on
+// 16x16x32 MFMAs (about 200 registers), and the 8 waves of a workgroup (128 keys of one (b, h_kv))
+// run in two groups in opposite matrix-core / VALU phases as in bwd_dkdv_pp_kernel:
+//   MFMA phase of step t: dV^T += dO^T P and dK^T += Q^T dS of step t - 1, then S and dP - D of
+//     step t (and this step's L into registers);
+//   VALU phase of step t: P and dS of step t, rounded as the next phase's B operands; group A also
+//     stages step t's dO^T / Q^T operands (below).
+// Per 64-row query tile and wave (query rows m, the wave's keys n):
+//   * S = Q K^T and dP - D = dO V^T - D: 4 blocks of 16 rows x 16 keys; A = Q (dO) rows read from
+//     LDS (row 16 qb + lane % 16, dims 32 ks + 8 (lane / 16) + [0, 8)), B = K (V) in registers. A
+//     lane holds rows 16 qb + 4 g + r (g = lane / 16, r < 4) of its key lane % 16.
+//   * dV^T += dO^T P, dK^T += Q^T dS: M = 16 dims, N = the 16 keys, K = 32 rows per k-step kk, in
+//     the k order that gives lane group g the rows 32 kk + 4 g + [0, 4) and 32 kk + 16 + 4 g +
+//     [0, 4): exactly the P (dS) values the lane holds, so the B operand is its own registers.
+//     Output block db holds dims 16 db + 4 g + r of key lane % 16.
+//   * Those A operands (dO^T, Q^T in that row order) are the same for all 8 waves: group A builds
+//     them once per tile in its VALU phase (two transposing LDS reads per fragment, wave gw the
+//     dim blocks 2 gw, 2 gw + 1), and every wave reads each with one 16-byte read. Read per wave
+//     with transposing reads, they were three quarters of the tile's LDS time.
+// Buffers (two of each): group A loads step t + 1's tiles and row vectors at the top of its MFMA
+// phase t, waits for them at the end of its VALU phase t; step t's tiles are read in the interval
+// of A's MFMA phase t (rows, A) and the next (rows, B; staging, A), its fragments in MFMA phases
+// t + 1 of both groups, and its L and -D rows in the MFMA phases t; each buffer is written only in
+// an interval after the barrier that ends the last one reading it.
+// ---------------------------------------------------------------------------------------------
+constexpr int k16Waves = 8;
+constexpr int k16Own = k16Waves * 16;            // keys per workgroup (= kOwn)
+
+template <typename T> struct Mma16;
+template <> struct Mma16<__bf16> {
+  static __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<_Float16> {
+  static __device__ __forceinline__ f32x4_t mma(f16x8_t a, f16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Issue order of a full MFMA phase of bwd_dkdv16_kernel (32 dV / dK MFMAs fed by one fragment read
+// each, then the 8 reads of -D and L, then 32 S / dP MFMAs fed by one row read each): the reads of
+// the MFMA PD positions ahead go before each MFMA. In the compiler's own order each MFMA waited
+// for the read just before it, so LDS latency showed on almost every one.
+__host__ __device__ constexpr int pp16_reads_needed(int i) { return i < 32 ? i + 1 : i + 9; }
+template <int PD, int I>
+__device__ __forceinline__ void dkdv16_order() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NM = 64;
+  constexpr int kMfma = 0x008, kDsRead = 0x100;  // sched_group_barrier instruction classes
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(kDsRead, pp16_reads_needed(PD), 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    constexpr int a = pp16_reads_needed(I + PD < NM ? I + PD : NM - 1);
+    constexpr int b = pp16_reads_needed(I + 1 + PD < NM ? I + 1 + PD : NM - 1);
+    if constexpr (b > a) __builtin_amdgcn_sched_group_barrier(kDsRead, b - a, 0);
+    dkdv16_order<PD, I + 1>();
+  }
+#endif
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(k16Waves * 64, 1) void bwd_dkdv16_kernel(BwdArgs a, int n_ktiles) {
+  constexpr int D = 128;
+  typedef BCfg<D, T> C;
+  typedef typename C::v8 v8;
+  constexpr int TB = 16 * D * (int)sizeof(T);    // bytes of 16 tile rows
+  __shared__ __attribute__((aligned(16))) T lds_q0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_q1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do0[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_do1[C::ELEMS];
+  __shared__ __attribute__((aligned(16))) float lds_l0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_l1[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d0[kTile];
+  __shared__ __attribute__((aligned(16))) float lds_d1[kTile];
+  // staged A operands of a step: fragment (tensor, kk, db) = 64 lanes x 16 bytes at
+  // ((tensor * 16 + kk * 8 + db) * 64 + lane) * 8, tensor 0 = dO^T, 1 = Q^T
+  __shared__ __attribute__((aligned(16))) T lds_f0[32 * 64 * 8];
+  __shared__ __attribute__((aligned(16))) T lds_f1[32 * 64 * 8];
+
+  // work order: see the file header (dK, dV)
+  int kt, rest;
+  if constexpr (CAUSAL) {
+    const int units = gridDim.x / n_ktiles;
+    kt = (int)blockIdx.x / units;
+    rest = (int)blockIdx.x % units;
+  } else {
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    kt = wg % n_ktiles;
+    rest = wg / n_ktiles;
+  }
+  const int hk = rest % a.H_kv;
+  const int b = rest / a.H_kv;
+  const int group = a.H / a.H_kv;
+  const size_t kvh = (size_t)b * a.H_kv + hk;
+  const T* __restrict__ K = static_cast<const T*>(a.k) + kvh * (size_t)a.Nk * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + kvh * (size_t)a.Nk * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool group_a = wave < 4;
+  const int gw = wave & 3;                       // wave index within its group (loads, staging: group A)
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int key = kt * k16Own + wave * 16 + n;   // this lane's key
+  const int keyc = min(key, a.Nk - 1);
+
+  // B operands of S and dP: K (V) row of this lane's key, dims 32 ks + 8 g + [0, 8)
+  v8 kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)keyc * D + ks * 32 + g * 8);
+    vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)keyc * D + ks * 32 + g * 8);
+  }
+  const float c2 = a.scale_log2e;
+
+  f32x4_t dk[8], dv[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dk[db][r] = dv[db][r] = 0.f;
+
+  const int n_rtiles = (a.Nq + kTile - 1) / kTile;
+  int r_begin = 0;
+  if constexpr (CAUSAL) r_begin = max(0, kt * k16Own - a.causal_off) / kTile;
+  const int per_head = n_rtiles - r_begin;
+  const int n_steps = per_head * group;          // (query head, row tile) pairs, head-major
+  auto row0 = [&](int st) { return (r_begin + st % per_head) * kTile; };
+
+  // Group A: a quarter of each tile per wave; wave 0 the lse rows, wave 1 the D rows.
+  auto issue = [&](int st, T* lq, T* ldo, float* ll, float* ld) __attribute__((always_inline)) {
+    const int h = hk * group + st / per_head;
+    const int r0 = row0(st);
+    const size_t head = (size_t)b * a.H + h;
+    load_tile<D, T>(static_cast<const T*>(a.q) + head * (size_t)a.Nq * D, lq, r0, a.Nq, gw, lane);
+    load_tile<D, T>(static_cast<const T*>(a.dout) + head * (size_t)a.Nq * D, ldo, r0, a.Nq, gw, lane);
+    if (wave == 0) load_rowvec(a.lse + head * a.Nq, ll, r0, a.Nq, lane);
+    if (wave == 1) load_rowvec(a.delta + head * a.Nq, ld, r0, a.Nq, lane);
+  };
+  // After the loads land (vmcnt(0) of the loading wave): lse * log2(e) (+inf past Nq), and -D.
+  auto prep_rows = [&](float* ll, float* ld, int r0) __attribute__((always_inline)) {
+    if (wave == 0) ll[lane] = r0 + lane < a.Nq ? ll[lane] * kLog2e : INFINITY;
+    if (wave == 1) ld[lane] = -ld[lane];
+  };
+
+  // Byte offsets of this lane's LDS reads within a tile. Row read (S, dP): row n (+ 16 qb), chunk
+  // 4 ks + g; the swizzle depends on row % 16 = n only. Transposing read for the staged fragment of
+  // k-step kk, half h, block db (group A, db = 2 gw + j): source lane n gives rows 32 kk + 16 h +
+  // 4 g + n / 4 (row % 16 = 4 g + n / 4), columns 16 db + 4 (n % 4) + [0, 4).
+  unsigned roff[4], toff[2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    roff[ks] = (unsigned)((n * D + (((4 * ks + g) ^ swz128(n)) << 3)) * sizeof(T));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tr = 4 * g + (n >> 2);
+    const int col = 16 * (2 * gw + j) + 4 * (n & 3);
+    toff[j] = (unsigned)((tr * D + (((col >> 3) ^ swz128(tr)) << 3) + (col & 7)) * sizeof(T));
+  }
+
+  f32x4_t s[4], dp[4];
+  f32x4_t Lr[4];                                 // this step's lse * log2(e) of the lane's rows
+  v8 pf[2], dsf[2];
+
+  // do_dkdv / do_sdp are compile-time flags (std::true_type / std::false_type)
+  auto phase_mfma = [&](int t, auto do_dkdv, auto do_sdp, const T* fprev, const T* qc, const T* doc,
+                        const float* lc, const float* dc, T* qn, T* don, float* ln, float* dn)
+      __attribute__((always_inline)) {
+    unsigned ro[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ro[i] = roff[i];
+      asm volatile("" : "+v"(ro[i]));
+    }
+    if (group_a && t + 1 < n_steps) issue(t + 1, qn, don, ln, dn);
+    if constexpr (decltype(do_dkdv)::value) {
+      // dV^T += dO^T P and dK^T += Q^T dS of step t - 1 (its staged fragments)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const v8 dof = *reinterpret_cast<const v8*>(&fprev[((kk * 8 + db) * 64 + lane) * 8]);
+          const v8 qf = *reinterpret_cast<const v8*>(&fprev[((16 + kk * 8 + db) * 64 + lane) * 8]);
+          dv[db] = Mma16<T>::mma(dof, pf[kk], dv[db]);
+          dk[db] = Mma16<T>::mma(qf, dsf[kk], dk[db]);
+        }
+    }
+    if constexpr (decltype(do_sdp)::value) {
+      // S and dP - D of step t (the dP accumulator starts at -D of rows 16 qb + 4 g + r)
+      const char* bq = reinterpret_cast<const char*>(qc);
+      const char* bdo = reinterpret_cast<const char*>(doc);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        s[qb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        dp[qb] = *reinterpret_cast<const f32x4_t*>(&dc[16 * qb + 4 * g]);
+        Lr[qb] = *reinterpret_cast<const f32x4_t*>(&lc[16 * qb + 4 * g]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          const int o = ro[ks] + qb * TB;
+          s[qb] = Mma16<T>::mma(*reinterpret_cast<const v8*>(bq + o), kf[ks], s[qb]);
+          dp[qb] = Mma16<T>::mma(*reinterpret_cast<const v8*>(bdo + o), vf[ks], dp[qb]);
+        }
+    }
+    // reads 16 MFMAs ahead (kernel time at the d = 128 backward workload: 1.24 ms at 6, 1.20 at 16)
+    if constexpr (decltype(do_dkdv)::value && decltype(do_sdp)::value) dkdv16_order<16, 0>();
+    __syncthreads();
+  };
+
+  auto phase_valu = [&](int t, const T* qc, const T* doc, T* fcur, float* ln, float* dn)
+      __attribute__((always_inline)) {
+    if (group_a) {
+      // step t's dO^T / Q^T fragments of dim blocks 2 gw, 2 gw + 1
+      unsigned to[2] = {toff[0], toff[1]};
+      asm volatile("" : "+v"(to[0]), "+v"(to[1]));
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        const char* bx = reinterpret_cast<const char*>(tq ? qc : doc);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int o1 = to[j] + 2 * kk * TB;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bx + o1));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(bx + o1 + TB));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+            const u32x4_t x = {l2[0], l2[1], h2[0], h2[1]};
+            *reinterpret_cast<u32x4_t*>(&fcur[((tq * 16 + kk * 8 + 2 * gw + j) * 64 + lane) * 8]) = x;
+          }
+      }
+    }
+    // P = 2^(s c - L log2 e) (0 past Nq through L = +inf), dS = P (dP - D). Under the causal mask
+    // the row 16 qb + 4 g + r of the tile sees this lane's key when 16 qb + 4 g + r >= key -
+    // causal_off - r0.
+    int lim = 0;
+    if constexpr (CAUSAL) lim = key - a.causal_off - row0(t) - 4 * g;
+    float p[4][4], ds[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lr[qb][r]));
+        if constexpr (CAUSAL) {
+          if (16 * qb + r < lim) x = 0.f;
+        }
+        p[qb][r] = x;
+        ds[qb][r] = x * dp[qb][r];
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[kk][i] = (T)p[2 * kk][i];
+        pf[kk][4 + i] = (T)p[2 * kk + 1][i];
+        dsf[kk][i] = (T)ds[2 * kk][i];
+        dsf[kk][4 + i] = (T)ds[2 * kk + 1][i];
+      }
+    if (group_a) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (t + 1 < n_steps) prep_rows(ln, dn, row0(t + 1));
+    }
+    __syncthreads();
+  };
+
+  // prologue: step 0's tiles resident and prepared; group B then sits out one phase
+  if (group_a && n_steps > 0) {
+    issue(0, lds_q0, lds_do0, lds_l0, lds_d0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    prep_rows(lds_l0, lds_d0, row0(0));
+  }
+  __syncthreads();
+  if (!group_a) __syncthreads();
+
+  // Step t reads tiles and rows t % 2 and fragments (t - 1) % 2, stages fragments t % 2 and loads
+  // into (t + 1) % 2. Every wave takes the same number of barriers.
+  const std::true_type yes;
+  const std::false_type no;
+  if (n_steps > 0) {
+    phase_mfma(0, no, yes, lds_f1, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+    phase_valu(0, lds_q0, lds_do0, lds_f0, lds_l1, lds_d1);
+  }
+  for (int t = 1; t < n_steps; t += 2) {
+    phase_mfma(t, yes, yes, lds_f0, lds_q1, lds_do1, lds_l1, lds_d1, lds_q0, lds_do0, lds_l0, lds_d0);
+    phase_valu(t, lds_q1, lds_do1, lds_f1, lds_l0, lds_d0);
+    if (t + 1 < n_steps) {
+      phase_mfma(t + 1, yes, yes, lds_f1, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+      phase_valu(t + 1, lds_q0, lds_do0, lds_f0, lds_l1, lds_d1);
+    }
+  }
+  if (n_steps == 0) phase_mfma(0, no, no, lds_f0, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+  else if ((n_steps - 1) % 2 == 0) phase_mfma(n_steps, yes, no, lds_f0, lds_q1, lds_do1, lds_l1, lds_d1, lds_q0, lds_do0, lds_l0, lds_d0);
+  else phase_mfma(n_steps, yes, no, lds_f1, lds_q0, lds_do0, lds_l0, lds_d0, lds_q1, lds_do1, lds_l1, lds_d1);
+  if (group_a) __syncthreads();
+
+  if (key < a.Nk) {
+    float* outk = a.dk + (kvh * (size_t)a.Nk + key) * D;
+    float* outv = a.dv + (kvh * (size_t)a.Nk + key) * D;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int dd = 16 * db + 4 * g;
+      f32x4_t xk = {a.scale * dk[db][0], a.scale * dk[db][1], a.scale * dk[db][2], a.scale * dk[db][3]};
+      *reinterpret_cast<f32x4_t*>(outk + dd) = xk;
+      *reinterpret_cast<f32x4_t*>(outv + dd) = dv[db];
+    }
+  }
+}
+
 template <int D, typename T>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.Nq;
@@ -1080,12 +1209,13 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_pp_kernel<T, true>)
                              : reinterpret_cast<const void*>(&bwd_dkdv_pp_kernel<T, false>);
     return hipLaunchKernel(k, dim3((unsigned)nkp), dim3(kPpWaves * 64), kargs, 0, s);
-  } else {
+  } else {  // d = 128: 16 keys per wave, two waves per SIMD (128 keys per workgroup, as kOwn)
+    static_assert(k16Own == kOwn, "the d = 128 dK dV grid uses n_ktiles of kOwn keys");
     int n = n_ktiles;
     void* kargs[] = {&args, &n};
-    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, true>)
-                             : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, T, false>);
-    return hipLaunchKernel(k, dim3((unsigned)nk), dim3(kBwdThreads), kargs, 0, s);
+    const void* k = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv16_kernel<T, true>)
+                             : reinterpret_cast<const void*>(&bwd_dkdv16_kernel<T, false>);
+    return hipLaunchKernel(k, dim3((unsigned)nk), dim3(k16Waves * 64), kargs, 0, s);
   }
 }
 
