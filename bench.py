@@ -43,7 +43,8 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # published fp32 vector peak (counts packed fp32 FMAs)
 MFMA_F32_PEAK_TFLOPS = 157.3    # published dense fp32 matrix-core peak
-EVENT_STRIDE = 4                # kernel launch timed by an event pair in every 4th timed step
+EVENT_STRIDE_MIN = 4            # kernel launch timed by an event pair in at most every 4th timed step,
+EVENT_SAMPLES = 16              # and in about 16 steps of a longer timed region
 HBM_PEAK_GBS = 8000.0
 METRIC = "FA fwd TFLOP/s (4*B*H*N^2*d) at N=4096,d=64 bf16; % of MFMA peak"
 
@@ -446,10 +447,11 @@ def main():
     # timed region: exactly K steps, synchronised on both sides
     ev_start = torch.cuda.Event(enable_timing=True)
     ev_end = torch.cuda.Event(enable_timing=True)
-    # an event pair around the dominant kernel's launch in every EVENT_STRIDE-th step of the timed region:
-    # its average launch duration (a timed event pair costs the stream several microseconds, which
-    # in every step would lengthen the steps of the short workloads by up to 15 %)
-    sampled = list(range(0, args.steps, EVENT_STRIDE))
+    # an event pair around the dominant kernel's launch in every stride-th step of the timed region:
+    # its average launch duration. A timed event pair costs the stream several microseconds: in every
+    # step it lengthened the 9 us single-head steps by 80 %, in every 4th by 15 %, in every 12th by 4 %.
+    stride = max(EVENT_STRIDE_MIN, args.steps // EVENT_SAMPLES)
+    sampled = list(range(0, args.steps, stride))
     kev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -466,7 +468,7 @@ def main():
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
     launch_stats = {"avg_launch_ms": avg_launch_ms, "median_launch_ms": launch_ms[len(launch_ms) // 2],
                     "min_launch_ms": launch_ms[0], "launches_timed": len(launch_ms),
-                    "launch_sampling": f"every {EVENT_STRIDE}th step of the timed region"}
+                    "launch_sampling": f"every {stride}th step of the timed region"}
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -520,14 +522,11 @@ def main():
             result.update({"metric": f"FA fwd microseconds per call at {what}", "unit": "us",
                            "value": ms_per_step * 1e3, "higher_is_better": False, "config": cfg,
                            "tflops": tflops})
-            if wname == "one_query":
-                result["roofline"] = {"bound": "alu", "kernel": "fwd_f32_rows_kernel", "achieved": achieved,
-                                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, **launch_stats, "traffic": None}
-            else:
-                result["roofline"] = {"bound": "mfma", "kernel": "fwd_f32_mfma_kernel", "achieved": achieved,
-                                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": achieved / MFMA_F32_PEAK_TFLOPS, **launch_stats, "traffic": None}
+            # both run on fwd_f32_rows_kernel (one workgroup per query row: 256 rows of one head at
+            # d = 64 is a launch it takes too)
+            result["roofline"] = {"bound": "alu", "kernel": "fwd_f32_rows_kernel", "achieved": achieved,
+                                  "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, **launch_stats, "traffic": None}
             if wname == "one_query":
                 result["split_path"] = time_split_one_query(torch, fa, q, k, v, o, wl.scale, stream)
         elif wname == "batched_queries":

@@ -101,6 +101,16 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H,
   return a;
 }
 
+// fp32: the one-workgroup-per-row kernel takes every call with at most 16 query rows, and also
+// small calls with more: it spreads the rows over the compute units, where a small launch of the
+// tiled kernels leaves most of them idle. Measured faster up to 256 rows per launch at d = 64
+// (B=H=1, N=256: 9.2 -> 8.3 us per call; 256 queries x 2048 keys: 27.7 -> 17.1 us) and up to 1024
+// at d = 128, where the tiled kernel is the VALU one (256 x 1024: 73 -> 16 us); slower beyond.
+bool f32_by_rows(const fa::FwdArgs& a, int d) {
+  const long long rows = (long long)a.B * a.H * a.Nq * a.num_splits;
+  return a.Nq <= fa::kDecodeMaxNq || rows <= (d == 64 ? 256 : 1024);
+}
+
 fa_status launched(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(FA_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return FA_OK;
@@ -148,7 +158,7 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
   a.out_dtype = out_dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (in_dtype == FA_F32) e = Nq <= fa::kDecodeMaxNq ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
+  if (in_dtype == FA_F32) e = f32_by_rows(a, d) ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
   else if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
   return launched(fn, e);
@@ -187,7 +197,7 @@ fa_status fwd_split_impl(const char* fn, const void* q, const void* k, const voi
   a.split_mode = lse_form ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (in_dtype == FA_F32) e = Nq <= fa::kDecodeMaxNq ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
+  if (in_dtype == FA_F32) e = f32_by_rows(a, d) ? fa::launch_fwd_f32_rows(a, d, s) : fa::launch_fwd_f32(a, d, s);
   else if (Nq <= fa::kDecodeMaxNq) e = fa::launch_decode(a, d, in_dtype, s);
   else e = fa::launch_fwd_mfma(a, d, in_dtype, s);
   return launched(fn, e);

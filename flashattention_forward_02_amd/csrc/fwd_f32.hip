@@ -2,7 +2,10 @@
 //  * fwd_f32_kernel (this header): more than 16 query rows at d = 128, on the VALU.
 //  * fwd_f32_mfma_kernel: more than 16 query rows at d = 64, the products on the fp32 matrix
 //    cores (described above it).
-//  * fwd_f32_rows_kernel: up to 16 query rows, keys spread over the lanes (described above it).
+//  * fwd_f32_rows_kernel: one workgroup per query row, keys spread over the lanes (described
+//    above it): calls of up to 16 query rows, and small calls of more (up to 256 rows per launch
+//    at d = 64, 1024 at d = 128), which it spreads over more compute units than the tiled
+//    kernels would use.
 //
 // fwd_f32_kernel. Same recurrence as the matrix-core kernel ("FlashAttention 简化版：Tiling + Online Softmax",
 // §2.3 and §3.1), written for accuracy: scores are s = scale * (q . k) in fp32, the running max
