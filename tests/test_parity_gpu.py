@@ -61,6 +61,29 @@ SMALL = [
 ]
 
 
+# fp32 launches of at most 256 rows (d = 64) or 1024 (d = 128) run one workgroup per row, larger
+# ones the tiled kernels: both sides of each limit, with and without the mask and the statistics.
+F32_LIMITS = [(1, 1, 256, 300, 64), (1, 1, 257, 300, 64), (1, 4, 256, 300, 128), (1, 4, 257, 300, 128),
+              (2, 2, 64, 129, 64), (1, 3, 100, 1000, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", F32_LIMITS, ids=lambda s: "x".join(map(str, s)))
+def test_fp32_kernel_choice_limits(shape, causal):
+    B, H, Nq, Nk, d = shape
+    say(f"fp32 kernel choice shape={shape} causal={causal}")
+    q, k, v = si.small_case(5000 + Nq + Nk + d, B, H, Nq, Nk, d, "f32")
+    scale = si.fp32_inverse_sqrt(d)
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    o, m, l = fa.fwd(qd, kd, vd, scale=scale, out_dtype=torch.float32, return_stats=True, causal=causal)
+    torch.cuda.synchronize()
+    ref, m_ref, l_ref = oracle.attention_fp64(q.as_f64(), k.as_f64(), v.as_f64(), scale, return_stats=True,
+                                              causal=causal)
+    assert_close(si.torch_to_f64(o), ref, "f32", f"fp32 {shape} causal={causal}")
+    assert_stats(si.torch_to_f64(m), si.torch_to_f64(l), m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), scale),
+                 f"fp32 {shape} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_small_shapes(dtype, shape):
