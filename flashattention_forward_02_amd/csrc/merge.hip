@@ -7,11 +7,12 @@
 // A state with m = -inf holds no keys and gets weight 0, so -inf - (-inf) is never evaluated.
 // The answer is o / l; a row whose states are all empty (l = 0) gets O = 0, as in the (lse, o) form.
 //
-// Layout: one thread per 4 columns of a row (C4 = d / 4 threads per row, 256 / C4 rows per
-// workgroup). The arithmetic is a sequential fold over the parts, but the loads are not: the
-// workgroup first stages the order and the row's per-part scalars (m and l, or lse) in LDS with
-// one parallel load each, then reads the parts' o vectors 8 at a time, so a row costs about
-// 2 + S / 8 memory round trips instead of one per part and scalar.
+// Layout: one thread per 4 columns of a row (C4 = d / 4 threads per row) and 64 threads per
+// workgroup (4 rows at d = 64, 2 at d = 128), so a few hundred rows still fill the chip. The
+// arithmetic is a sequential fold over the parts, but the loads are not: the workgroup stages the
+// order and its rows' per-part scalars (m and l, or lse, in part-index order) in LDS in one round
+// of loads, then reads the parts' o vectors 16 at a time in fold order, so a row costs about
+// 1 + S / 16 memory round trips instead of one per part and scalar.
 
 #include "fa_internal.h"
 
@@ -42,8 +43,9 @@ __device__ __forceinline__ void store_o4(void* o, size_t e, int out_dtype, const
 template <int D>
 struct MergeCfg {
   static constexpr int C4 = D / 4;        // threads per row
-  static constexpr int RPB = 256 / C4;    // rows per workgroup
-  static constexpr int U = 8;             // partial o vectors in flight per thread
+  static constexpr int NT = 64;           // threads per workgroup
+  static constexpr int RPB = NT / C4;     // rows per workgroup
+  static constexpr int U = 16;            // partial o vectors in flight per thread
 };
 
 // Dynamic LDS of a merge workgroup: order[S], then per row NV * S scalars.
@@ -52,30 +54,41 @@ inline size_t merge_lds_bytes(int S, int nv) {
   return ((size_t)S + (size_t)MergeCfg<D>::RPB * nv * S) * sizeof(float);
 }
 
-// Stages order[] and the row's per-part scalars (x0, and x1 when NV = 2), in fold order, in LDS.
-// Returns false for the threads of rows past the end (after the workgroup barrier).
+// Stages order[] and the workgroup's rows' per-part scalars (x0, and x1 when NV = 2) in LDS, the
+// scalars in part-index order (none of these loads waits for another); s0 / s1 point at this
+// thread's row. Returns false for the threads of rows past the end (after the workgroup barrier).
 template <int D, int NV>
-__device__ __forceinline__ bool stage_scalars(const MergeArgs& a, float* sh, long long row, int c4,
-                                              const float* x0, const float* x1, float*& s0, float*& s1) {
+__device__ __forceinline__ bool stage_scalars(const MergeArgs& a, float* sh, long long row0, const float* x0,
+                                              const float* x1, float*& s0, float*& s1) {
   typedef MergeCfg<D> C;
   const int S = a.S;
   int* sh_order = reinterpret_cast<int*>(sh);
-  for (int k = threadIdx.x; k < S; k += 256) sh_order[k] = a.order[k];
+  // item i: order[i] (i < S), and the scalars of part i / RPB of row row0 + i % RPB (consecutive
+  // threads read consecutive rows); both loads of an item are issued before either is written
+#pragma unroll 2
+  for (int i = threadIdx.x; i < S * C::RPB; i += C::NT) {
+    const int part = i / C::RPB, lr = i % C::RPB;
+    const bool has_order = i < S, has_row = row0 + lr < a.rows;
+    const size_t p = (size_t)part * a.rows + row0 + lr;
+    int ord = 0;
+    float v0 = 0.f, v1 = 0.f;
+    if (has_order) ord = a.order[i];
+    if (has_row) {
+      v0 = x0[p];
+      if constexpr (NV == 2) v1 = x1[p];
+    }
+    if (has_order) sh_order[i] = ord;
+    if (has_row) {
+      float* dst = sh + S + (size_t)lr * NV * S + part;
+      dst[0] = v0;
+      if constexpr (NV == 2) dst[S] = v1;
+    }
+  }
   __syncthreads();
   const int lr = threadIdx.x / C::C4;
   s0 = sh + S + (size_t)lr * NV * S;
   s1 = s0 + S;
-  const bool live = row < a.rows;
-  if (live) {
-#pragma unroll 4
-    for (int k = c4; k < S; k += C::C4) {
-      const size_t p = (size_t)sh_order[k] * a.rows + row;
-      s0[k] = x0[p];
-      if constexpr (NV == 2) s1[k] = x1[p];
-    }
-  }
-  __syncthreads();
-  return live;
+  return row0 + lr < a.rows;
 }
 
 // The row's o vectors of parts k0 .. k0 + U - 1 (in fold order; positions past S repeat part S - 1).
@@ -91,14 +104,15 @@ __device__ __forceinline__ void load_parts(const MergeArgs& a, const int* sh_ord
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(MergeCfg<D>::NT) void merge_kernel(MergeArgs a) {
   typedef MergeCfg<D> C;
   extern __shared__ float sh[];
   const int c4 = threadIdx.x % C::C4;
   const int c = c4 * 4;
-  const long long row = (long long)blockIdx.x * C::RPB + threadIdx.x / C::C4;
+  const long long row0 = (long long)blockIdx.x * C::RPB;
+  const long long row = row0 + threadIdx.x / C::C4;
   float *sm, *sl;
-  if (!stage_scalars<D, 2>(a, sh, row, c4, a.part_m, a.part_l, sm, sl)) return;
+  if (!stage_scalars<D, 2>(a, sh, row0, a.part_m, a.part_l, sm, sl)) return;
   const int* sh_order = reinterpret_cast<const int*>(sh);
 
   float m = -INFINITY, l = 0.f;
@@ -109,7 +123,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       if (k0 + u >= a.S) break;
-      const float ms = sm[k0 + u], ls = sl[k0 + u];
+      const int part = sh_order[k0 + u];
+      const float ms = sm[part], ls = sl[part];
       const float mn = fmaxf(m, ms);
       const float wa = weight(m, mn), wb = weight(ms, mn);
       l = l * wa + ls * wb;
@@ -133,22 +148,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 // of exp(lse_s - max)). Parts with lse_s = -inf (no keys) weigh 0; a row whose parts are all
 // empty gets O = 0 and lse = -inf. Sums run in the caller's order.
 template <int D>
-__global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
+__global__ __launch_bounds__(MergeCfg<D>::NT) void merge_lse_kernel(MergeArgs a) {
   typedef MergeCfg<D> C;
   extern __shared__ float sh[];
   const int c4 = threadIdx.x % C::C4;
   const int c = c4 * 4;
-  const long long row = (long long)blockIdx.x * C::RPB + threadIdx.x / C::C4;
+  const long long row0 = (long long)blockIdx.x * C::RPB;
+  const long long row = row0 + threadIdx.x / C::C4;
   float *sl, *unused;
-  if (!stage_scalars<D, 1>(a, sh, row, c4, a.part_m, nullptr, sl, unused)) return;
+  if (!stage_scalars<D, 1>(a, sh, row0, a.part_m, nullptr, sl, unused)) return;
   const int* sh_order = reinterpret_cast<const int*>(sh);
 
   float mx = -INFINITY;
-  for (int k = 0; k < a.S; ++k) mx = fmaxf(mx, sl[k]);
+  for (int k = 0; k < a.S; ++k) mx = fmaxf(mx, sl[sh_order[k]]);
   float sum = 0.f;
   if (mx != -INFINITY) {
     for (int k = 0; k < a.S; ++k) {
-      const float ls = sl[k];
+      const float ls = sl[sh_order[k]];
       if (ls != -INFINITY) sum += expf(ls - mx);
     }
   }
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 #pragma unroll
       for (int u = 0; u < C::U; ++u) {
         if (k0 + u >= a.S) break;
-        const float ls = sl[k0 + u];
+        const float ls = sl[sh_order[k0 + u]];
         if (ls == -INFINITY) continue;
         const float w = expf(ls - lse);
 #pragma unroll
@@ -182,7 +198,7 @@ hipError_t launch_typed(const MergeArgs& a, hipStream_t s) {
   const void* k = a.lse_format ? reinterpret_cast<const void*>(&merge_lse_kernel<D>)
                                : reinterpret_cast<const void*>(&merge_kernel<D>);
   const size_t lds = merge_lds_bytes<D>(a.S, a.lse_format ? 1 : 2);
-  return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), kargs, lds, s);
+  return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(MergeCfg<D>::NT), kargs, lds, s);
 }
 
 }  // namespace
