@@ -491,9 +491,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
   if constexpr (CAUSAL) kend = min(kend, min(a.Nq, (qt + 1) * C::BR) + a.causal_off);
   const int nkeys = kend - kbeg;
   const int T_ = nkeys > 0 ? (nkeys + kBC - 1) / kBC : 0;  // key tiles
-  // Tiles [0, n_plain) hold only keys every row of the workgroup sees: no masking there.
+  // Tiles [0, n_plain) hold only keys every row of the wave sees: no masking there (under the
+  // causal mask the bound is per wave, set below).
   int n_plain = (nkeys % kBC == 0) ? T_ : T_ - 1;
-  if constexpr (CAUSAL) n_plain = min(n_plain, max(0, (qt * C::BR + a.causal_off + 1 - kbeg) / kBC));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -556,6 +556,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
     if constexpr (CAUSAL) return wave_row0 + NB * 32 + a.causal_off <= kbeg + t * kBC;
     else return false;
   };
+  // Causal: the tiles whose keys the wave's first row (and so every row of the wave) sees in
+  // full. A wave further down the query tile sees more of the diagonal tiles in full than the
+  // workgroup's first row does; it takes the unmasked softmax there. Every wave runs the same
+  // barriers per tile on either path.
+  if constexpr (CAUSAL) n_plain = min(n_plain, max(0, (wave_row0 + a.causal_off + 1 - kbeg) / kBC));
 
   // ---- the two phases of one tile ----
   // Loads (group A only; global -> LDS, asynchronous). Staged: K(t+1) and V(t+1) start at the top
