@@ -29,10 +29,20 @@ template <> struct Mma<_Float16> {
   }
 };
 
+// Maxima of scores (finite, or -inf for masked ones). fmaxf would first quiet a possible
+// signalling NaN in every operand the compiler cannot prove canonical (one extra v_max_f32 x, x
+// per operand, and an MFMA result is such an operand), which doubles the cost of a row maximum.
+// The NaN-propagating maximum needs no quieting and becomes v_maximum3_f32 on gfx950, two new
+// values per instruction; for scores it is the same maximum.
+__device__ __forceinline__ float max2f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // Max / sum of a value and its counterpart in the other half of the wave (lane l and l ^ 32).
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
