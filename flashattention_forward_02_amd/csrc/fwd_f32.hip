@@ -321,7 +321,7 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
 // Max / sum over the 4 lanes that hold one query (lanes 16 apart).
 __device__ __forceinline__ float qrow_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return xhalf_max(max2f(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 __device__ __forceinline__ float qrow_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -444,11 +444,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_mfma_kernel(FwdArgs a, int n_
   auto update = [&](int t, const f32x4_t& s, const float (&vx)[16]) {
     const int key0 = kbeg + t * kKM;
     const bool full = key0 + kKM <= all_end;   // every key of the step is seen by every row
-    float mt = -INFINITY;
+    float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (full || key0 + 4 * g + r < row_end) mt = fmaxf(mt, s[r]);
-    mt = qrow_max(mt);
+    for (int r = 0; r < 4; ++r) sv[r] = (full || key0 + 4 * g + r < row_end) ? s[r] : -INFINITY;
+    float mt = qrow_max(max3f(sv[0], sv[1], max2f(sv[2], sv[3])));
     const bool grow = mt > mraw;             // false while the query has seen no key (both -inf)
     if (__ballot(grow)) {                    // rescale l and the accumulators by 2^(m2_old - m2_new)
       const float m2new = grow ? mt * c : m2;
