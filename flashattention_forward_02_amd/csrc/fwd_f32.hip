@@ -383,14 +383,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_mfma_kernel(FwdArgs a, int n_
   // first key row: K n * 256 + g * 16 (+ 64 G), V 4 g * 256 + n * 16 (+ 256 kk).
   const unsigned koffb = (unsigned)(n * 256 + g * 16);
   const unsigned voffb = (unsigned)(g * 1024 + n * 16);
-  // Buffer loads: the descriptor of a step starts at its first key row and holds the rows up to
-  // kend, so the rows of a ragged last step that lie past kend read as 0 (the hardware's range
-  // check; their scores are masked) and no load branches. Steps past the wave's last one are
-  // clamped to it (those loads are not used).
+  // Buffer loads: the descriptor of a step starts at its first key row (a 64-bit address) and
+  // holds that step's rows only, at most 16 (4 KB, so the 32-bit record count never overflows,
+  // whatever Nk is), so the rows of a ragged last step that lie past kend read as 0 (the
+  // hardware's range check; their scores are masked) and no load branches. Steps past the wave's
+  // last one are clamped to it (those loads are not used).
   auto step_rsrc = [&](const float* X, int t) {
     const int key0 = kbeg + min(t, t1 - 1) * kKM;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(X + (size_t)key0 * D), 0,
-                                             (kend - key0) * D * (int)sizeof(float), kBufferWord3);
+                                             min(kend - key0, kKM) * D * (int)sizeof(float), kBufferWord3);
   };
   auto load_k = [&](int t, float (&kx)[16]) {
     const __amdgpu_buffer_rsrc_t r = step_rsrc(K, t);
@@ -835,8 +836,7 @@ hipError_t launch_fwd_f32_mfma(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s) {
-  // the matrix-core kernel's buffer descriptors count a key range in bytes in 32 bits
-  if (d == 64 && (long long)a.Nk * 64 * (long long)sizeof(float) <= 0x7fffffffLL) return launch_fwd_f32_mfma(a, s);
+  if (d == 64) return launch_fwd_f32_mfma(a, s);
   if (d == 128) return launch_typed<128>(a, s);
   return hipErrorInvalidValue;
 }

@@ -245,6 +245,28 @@ def test_single_head_fp32_256x64():
     assert_stats(m, l, m_ref, l_ref, stat_bound(q.as_f64(), k.as_f64(), 0.125))
 
 
+def test_fp32_key_range_past_2gib():
+    """fp32 at d = 64 with 8388645 keys: K and V each span more than 2^31 bytes (past what a 32-bit
+    byte count covers), and 300 query rows take the matrix-core kernel. Three rows against the
+    oracle; Q, K, V drawn on the device (seeds 7001, 7002, 7003)."""
+    B, H, Nq, Nk, d = 1, 1, 300, 8388645, 64
+    say("fp32 key range past 2 GiB: drawing 4.3 GB of K and V on the device")
+    q = si.device_draw((B, H, Nq, d), 7001, "f32", DEV)
+    k = si.device_draw((B, H, Nk, d), 7002, "f32", DEV)
+    v = si.device_draw((B, H, Nk, d), 7003, "f32", DEV)
+    o, m, l = fa.fwd(q, k, v, scale=0.125, out_dtype=torch.float32, return_stats=True)
+    torch.cuda.synchronize()
+    say("fp32 key range past 2 GiB: oracle on 3 rows")
+    rows = np.array([0, 151, 299])
+    qh = si.torch_to_f64(q[0, 0])[rows]
+    kh, vh = si.torch_to_f64(k[0, 0]), si.torch_to_f64(v[0, 0])
+    del k, v
+    ref, m_ref, l_ref = oracle.attention_rows_fp64(qh, kh, vh, 0.125)
+    assert_close(si.torch_to_f64(o[0, 0])[rows], ref, "f32", "fp32 key range past 2 GiB")
+    assert_stats(si.torch_to_f64(m[0, 0])[rows], si.torch_to_f64(l[0, 0])[rows], m_ref, l_ref,
+                 stat_bound(qh, kh, 0.125), "fp32 key range past 2 GiB")
+
+
 @pytest.mark.parametrize("batched", [False, True])
 def test_one_query_long_keys_fp32(batched):
     say(f"one_query_long_keys batched={batched}")
