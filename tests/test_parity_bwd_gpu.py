@@ -80,6 +80,11 @@ CASES = [
     (1, 2, 2, 64, 64, 64, False),
     (1, 2, 2, 128, 192, 64, True),
     (1, 1, 1, 192, 128, 64, False),
+    # d = 128: 1, 2 and 3 blocks of 128 keys (dK dV, two buffers) and of 64-row steps, grouped heads
+    (1, 2, 2, 64, 128, 128, False),
+    (1, 2, 1, 128, 256, 128, True),
+    (1, 1, 1, 192, 384, 128, False),
+    (1, 4, 1, 130, 260, 128, False),
 ]
 
 
@@ -145,6 +150,23 @@ def test_backward_headline_shape_sampled_heads():
                                                                 do.as_f64()[sl], w.scale)
         for name, got, ref in (("dq", dq[sl], rdq), ("dk", dk[sl], rdk), ("dv", dv[sl], rdv)):
             ma, rl = assert_grad_close(got, ref, "bf16", f"headline {name} head {(b, h)}")
+            say(f"  head {(b, h)} {name}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+
+
+def test_backward_d128_workload_sampled_heads():
+    """The d = 128 backward workload (B=4, H=16, N=4096, d=128 bf16; seed 3, dO = tensor 3), the launch
+    bench.py times: every head runs on the GPU; the oracle checks two heads in full."""
+    w = si.BWD_D128_BF16
+    q, k, v = si.workload_inputs(w)
+    do = si.grad_output(w)
+    say("bwd d=128 workload")
+    o, lse, dq, dk, dv, delta = run_gpu(q, k, v, do, w.scale, False)
+    for (b, h) in ((0, 7), (3, 12)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rdq, rdk, rdv, rlse, _ = oracle.attention_backward_fp64(q.as_f64()[sl], k.as_f64()[sl], v.as_f64()[sl],
+                                                                do.as_f64()[sl], w.scale)
+        for name, got, ref in (("dq", dq[sl], rdq), ("dk", dk[sl], rdk), ("dv", dv[sl], rdv)):
+            ma, rl = assert_grad_close(got, ref, "bf16", f"d128 workload {name} head {(b, h)}")
             say(f"  head {(b, h)} {name}: max_abs={ma:.3e} rel_l2={rl:.3e}")
 
 
