@@ -126,6 +126,30 @@ def test_key_tile_counts(case, d, stats):
     assert_close(o, ref, "bf16", f"tiles {case} d={d} stats={stats}")
 
 
+# No kernel uses atomics or an order that depends on timing, so repeated calls give identical bits.
+DETERMINISM = [("bf16", (2, 4, 700, 900, 64), False), ("bf16", (1, 3, 300, 500, 128), True), ("f32", (1, 1, 256, 300, 64), False),
+               ("f32", (1, 2, 300, 400, 64), True), ("f32", (1, 2, 600, 300, 128), False), ("bf16", (2, 4, 1, 5000, 128), False)]
+
+
+@pytest.mark.parametrize("case", DETERMINISM, ids=lambda c: f"{c[0]}-{'x'.join(map(str, c[1]))}{'c' if c[2] else ''}")
+def test_forward_is_bitwise_repeatable(case):
+    dtype, (B, H, Nq, Nk, d), causal = case
+    say(f"determinism dtype={dtype} shape={(B, H, Nq, Nk, d)} causal={causal}")
+    q, k, v = si.small_case(6000 + Nq + Nk + d, B, H, Nq, Nk, d, dtype)
+    qd, kd, vd = q.to_torch(DEV), k.to_torch(DEV), v.to_torch(DEV)
+    runs = []
+    for _ in range(3):
+        o, m, l = fa.fwd(qd, kd, vd, out_dtype=torch.float32, return_stats=True, causal=causal)
+        o_only = fa.fwd(qd, kd, vd, out_dtype=torch.float32, causal=causal)
+        ps = fa.fwd_split_lse(qd, kd, vd, 7, causal=causal)
+        om = fa.merge_lse(*ps, order=list(range(7))[::-1], return_lse=False)
+        torch.cuda.synchronize()
+        runs.append([t.cpu().numpy() for t in (o, m, l, o_only, om)])
+    for r in runs[1:]:
+        for x, y in zip(runs[0], r):
+            assert np.array_equal(x, y, equal_nan=True)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_low_precision_output_dtype(dtype):
     q, k, v = si.small_case(77, 2, 2, 300, 500, 64, dtype)
