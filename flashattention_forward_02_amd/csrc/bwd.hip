@@ -524,6 +524,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
     const int r0 = row0(t);
     int lim = 0;
     if constexpr (CAUSAL) lim = key - a.causal_off - r0 - 4 * hf;
+    auto grads = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qb = g >> 1;
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g4 + u;
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, -Lv[u]));
-          if constexpr (CAUSAL) {
+          if constexpr (decltype(masked)::value) {
             if (32 * qb + 8 * g4 + u < lim) x = 0.f;
           }
           p[4 * h2 + u] = x;
@@ -546,6 +547,10 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void bwd_dkdv_pp_kernel(BwdArgs a
       pf[g] = pack8<T>(p);
       dsf[g] = pack8<T>(ds);
     }
+    };
+    // the per-key mask only where the wave's last key lies past what the step's first row sees
+    if (CAUSAL && kt * kPpOwn + wave * 32 + 31 > r0 + a.causal_off) grads(std::true_type());
+    else grads(std::false_type());
     if (group_a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (t + 1 < n_steps) prep_rows(ln, dn, row0(t + 1));
