@@ -329,8 +329,8 @@ def time_split_one_query(torch, fa, q, k, v, o_ref, scale, stream, S=16, calls=2
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not implemented "
-                                   "(heads shard across GPUs with no exchange; see the design notes)"}))
+        print(json.dumps({"error": "bench.py runs on one GPU only; multi-GPU runs are not implemented "
+                                   "(heads shard across GPUs with no exchange)"}))
         sys.exit(2)
     wname = args.workload
     if wname == "headline_literal":

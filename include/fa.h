@@ -34,7 +34,7 @@
  *   - All calls are asynchronous on `stream` (a hipStream_t; NULL means the null stream).
  *   - Errors: every call validates its arguments on the host before touching the device and
  *     returns a status; nothing aborts, throws or prints. FA_EINVAL: a bad pointer, size,
- *     dtype, scale or alignment. FA_EUNSUPPORTED: a valid request this build does not
+ *     dtype, scale or alignment. FA_EUNSUPPORTED: a valid request the library does not
  *     implement (e.g. d = 96). FA_EHIP: the HIP runtime reported an error when launching.
  *     fa_last_error() then returns a description (per thread, valid until the next call).
  *     B*H = 0 or Nq = 0 is a successful no-op. Nk must be >= 1 (softmax over no keys is
