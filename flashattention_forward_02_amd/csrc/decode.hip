@@ -15,6 +15,14 @@
 //
 // These kernels take bf16 / fp16 inputs and use base-2 scores, exp(s - m) = 2^(raw*c - m*c) with
 // c = scale*log2(e); fp32 rows go to the fp32 kernels.
+//
+// decode_rows_kernel (R rows sharing each K/V load) has four times the softmax work per byte of
+// decode_kernel, so it keeps its exponentials relative to a reference that moves to the running
+// maximum only when the maximum passes it by more than tau (as the tiled kernel does): most keys
+// then cost one FMA and one exponential per row, and the rescaling of l and the accumulator is a
+// rare, wave-uniform branch; at the end l and the accumulator are re-expressed relative to the
+// true maximum, so the partial states are the same (m, l, o) as the plain recurrence gives, up to
+// rounding. With one key per group step it also loads each step's K and V words one step ahead.
 
 #include <type_traits>
 
@@ -222,17 +230,52 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
   }
   const float c2 = a.scale_log2e;
 
-  float m[R], l[R], acc[R][DL];
+  // m: the running maximum of the raw scores; ref: the exponent reference (base-2 units), moved
+  // to the maximum only when the maximum passes it by more than tau, as in the tiled kernel
+  const float tau = a.rescale_threshold;
+  float m[R], ref[R], l[R], acc[R][DL];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     m[j] = -INFINITY;
+    ref[j] = -INFINITY;
     l[j] = 0.f;
 #pragma unroll
     for (int c = 0; c < DL; ++c) acc[j][c] = 0.f;
   }
 
+  // one key per group step (U = 1, d = 128): its K and V words are loaded one step ahead
+  u32x4_t kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+  if constexpr (U == 1 && DL == 8) {
+    const int key = kbeg + g;
+    if (key < kend) {
+      kn = *reinterpret_cast<const u32x4_t*>(K + (size_t)key * D);
+      vn = *reinterpret_cast<const u32x4_t*>(V + (size_t)key * D);
+    }
+  }
   for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
     float kx[U][DL], vx[U][DL];
+    if constexpr (U == 1 && DL == 8) {
+      const u32x4_t kc = kn, vc = vn;
+      const int nk = base + kGroups;
+      if (nk < kend) {
+        kn = *reinterpret_cast<const u32x4_t*>(K + (size_t)nk * D);
+        vn = *reinterpret_cast<const u32x4_t*>(V + (size_t)nk * D);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (std::is_same<T, __bf16>::value) {
+          kx[0][2 * i] = __uint_as_float(kc[i] << 16);
+          kx[0][2 * i + 1] = __uint_as_float(kc[i] & 0xffff0000u);
+          vx[0][2 * i] = __uint_as_float(vc[i] << 16);
+          vx[0][2 * i + 1] = __uint_as_float(vc[i] & 0xffff0000u);
+        } else {
+          kx[0][2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(kc[i] & 0xffffu));
+          kx[0][2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(kc[i] >> 16));
+          vx[0][2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(vc[i] & 0xffffu));
+          vx[0][2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(vc[i] >> 16));
+        }
+      }
+    } else {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = base + u;
@@ -243,6 +286,7 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;
       }
+    }
     }
     float sc[U][R];
 #pragma unroll
@@ -283,26 +327,46 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
         }
       }
     }
+    bool move = false;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      float mx = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
-      const float mnew = fmaxf(m[j], mx);
-      const float alpha = (m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[j] - mnew) * c2);
-      l[j] *= alpha;
+      for (int u = 0; u < U; ++u) m[j] = fmaxf(m[j], sc[u][j]);
+      const float mc = (m[j] == -INFINITY) ? -INFINITY : m[j] * c2;
+      move |= mc > ref[j] + tau;
+    }
+    if (__ballot(move)) {
 #pragma unroll
-      for (int c = 0; c < DL; ++c) acc[j][c] *= alpha;
+      for (int j = 0; j < R; ++j) {
+        const float mc = (m[j] == -INFINITY) ? -INFINITY : m[j] * c2;
+        const float nref = (mc > ref[j] + tau) ? mc : ref[j];
+        const float alpha = (ref[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ref[j] - nref);
+        l[j] *= alpha;
+#pragma unroll
+        for (int c = 0; c < DL; ++c) acc[j][c] *= alpha;
+        ref[j] = nref;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][j], c2, -mnew * c2));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][j], c2, -ref[j]));
         if (sc[u][j] == -INFINITY) p = 0.f;
         l[j] += p;
 #pragma unroll
         for (int c = 0; c < DL; ++c) acc[j][c] = __builtin_fmaf(p, vx[u][c], acc[j][c]);
       }
-      m[j] = mnew;
     }
+  }
+  // l and acc relative to the true maximum
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const float mc = (m[j] == -INFINITY) ? -INFINITY : m[j] * c2;
+    const float f = (ref[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ref[j] - mc);
+    l[j] *= f;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) acc[j][c] *= f;
   }
 
   // ---- merge the 16 group states of each row (as in decode_kernel) ----
