@@ -272,21 +272,21 @@ def run_probes(torch, fa, stream):
         best = t if best is None else min(best, t)
     res["mfma_f32_tflops"] = flops / (best * 1e-3) / 1e12
     buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
-    rout = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
-    nbytes = fa.probe_hbm_read(buf, nblocks=4096, out=rout)
+    rout = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
+    nbytes = fa.probe_hbm_read(buf, nblocks=1024, out=rout)
     torch.cuda.synchronize()
     best = None
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        fa.probe_hbm_read(buf, nblocks=4096, out=rout)
+        fa.probe_hbm_read(buf, nblocks=1024, out=rout)
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1)
         best = t if best is None else min(best, t)
     res["hbm_read_gbs"] = nbytes / (best * 1e-3) / 1e9
     res["what"] = ("fa_probe_mfma_bf16 (2048 workgroups x 4 waves x 1024 x 8 MFMAs 32x32x16), fa_probe_mfma_f32 "
-                   "(2048 x 4 waves x 256 x 8 MFMAs 16x16x4 fp32) and fa_probe_hbm_read (4 GiB, 16-byte loads), "
+                   "(2048 x 4 waves x 256 x 8 MFMAs 16x16x4 fp32) and fa_probe_hbm_read (4 GiB in 1024 contiguous 4 MiB chunks, nontemporal 16-byte loads), "
                    "best of 5 launches each")
     del buf
     return res

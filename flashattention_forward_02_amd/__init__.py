@@ -273,7 +273,7 @@ def probe_mfma_f32(nblocks=2048, iters=1024, out=None):
     return float(nblocks) * 4 * iters * 8 * 2048, out
 
 
-def probe_hbm_read(buf, nblocks=4096, out=None):
+def probe_hbm_read(buf, nblocks=1024, out=None):
     """Launch the streaming-read probe of fa_probe.h over every byte of the device tensor ``buf``; returns the
     number of bytes read. ``out`` (optional) is an int32 device tensor of at least nblocks * 256 elements."""
     torch = _torch()

@@ -23,6 +23,9 @@
 // rare, wave-uniform branch; at the end l and the accumulator are re-expressed relative to the
 // true maximum, so the partial states are the same (m, l, o) as the plain recurrence gives, up to
 // rounding. With one key per group step it also loads each step's K and V words one step ahead.
+//
+// K and V are read once, so their loads are nontemporal: 1415 -> 1258 us on B=16, H=32,
+// Nk=32768, d=128 split 16 ways (6.07 -> 6.83 TB/s of K and V), 369 -> 342 us with 8 K/V heads.
 
 #include <type_traits>
 
@@ -38,15 +41,15 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 // Load N consecutive bf16 / fp16 elements and widen them to fp32.
-template <typename T, int N>
+template <typename T, int N, bool NT = false>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[N]) {
   static_assert(N == 4 || N == 8, "");
   unsigned w[N / 2];
   if constexpr (N == 8) {
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)) : *reinterpret_cast<const u32x4_t*>(p);
     w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
   } else {
-    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t x = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)) : *reinterpret_cast<const u32x2_t*>(p);
     w[0] = x[0]; w[1] = x[1];
   }
 #pragma unroll
@@ -107,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int key = base + u;
       if (key < kend) {
-        load_row<T, DL>(K + (size_t)key * D, kx[u]);
-        load_row<T, DL>(V + (size_t)key * D, vx[u]);
+        load_row<T, DL, true>(K + (size_t)key * D, kx[u]);
+        load_row<T, DL, true>(V + (size_t)key * D, vx[u]);
       } else {
 #pragma unroll
         for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
   if constexpr (U == 1 && DL == 8) {
     const int key = kbeg + g;
     if (key < kend) {
-      kn = *reinterpret_cast<const u32x4_t*>(K + (size_t)key * D);
-      vn = *reinterpret_cast<const u32x4_t*>(V + (size_t)key * D);
+      kn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(K + (size_t)key * D));
+      vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(V + (size_t)key * D));
     }
   }
   for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
@@ -258,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
       const u32x4_t kc = kn, vc = vn;
       const int nk = base + kGroups;
       if (nk < kend) {
-        kn = *reinterpret_cast<const u32x4_t*>(K + (size_t)nk * D);
-        vn = *reinterpret_cast<const u32x4_t*>(V + (size_t)nk * D);
+        kn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(K + (size_t)nk * D));
+        vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(V + (size_t)nk * D));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int key = base + u;
       if (key < kend) {
-        load_row<T, DL>(K + (size_t)key * D, kx[u]);
-        load_row<T, DL>(V + (size_t)key * D, vx[u]);
+        load_row<T, DL, true>(K + (size_t)key * D, kx[u]);
+        load_row<T, DL, true>(V + (size_t)key * D, vx[u]);
       } else {
 #pragma unroll
         for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;

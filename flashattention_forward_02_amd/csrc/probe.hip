@@ -65,25 +65,26 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_f32_kernel(float* __
 
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ src, size_t n16,
                                                                     unsigned* __restrict__ out) {
-  const size_t stride = (size_t)gridDim.x * kProbeThreads;
-  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  // Workgroup b reads the contiguous words [b n16 / nb, (b + 1) n16 / nb) with nontemporal 16-byte
+  // loads, eight in flight per lane (of the patterns measured, contiguous per-workgroup chunks of
+  // 1-4 MB read this way streamed fastest); the tail loop takes what is left of the chunk.
+  const size_t nb = gridDim.x;
+  const size_t end = n16 * (blockIdx.x + 1) / nb;
+  size_t i = n16 * blockIdx.x / nb + threadIdx.x;
   unsigned x = 0u;
-  // four independent loads in flight per lane; the tail loop takes what is left
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_t v0 = __builtin_nontemporal_load(&src[i]);
-    const u32x4_t v1 = __builtin_nontemporal_load(&src[i + stride]);
-    const u32x4_t v2 = __builtin_nontemporal_load(&src[i + 2 * stride]);
-    const u32x4_t v3 = __builtin_nontemporal_load(&src[i + 3 * stride]);
-    x ^= (v0[0] ^ v0[1] ^ v0[2] ^ v0[3]) ^ (v1[0] ^ v1[1] ^ v1[2] ^ v1[3]) ^ (v2[0] ^ v2[1] ^ v2[2] ^ v2[3]) ^
-         (v3[0] ^ v3[1] ^ v3[2] ^ v3[3]);
+  for (; i + 7 * kProbeThreads < end; i += 8 * kProbeThreads) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * kProbeThreads]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += kProbeThreads) {
     const u32x4_t v = __builtin_nontemporal_load(&src[i]);
     x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = x;
 }
-
 }  // namespace
 
 hipError_t launch_probe_mfma(float* out, int nblocks, int iters, hipStream_t s) {

@@ -37,8 +37,9 @@ fa_status fa_probe_mfma_f32(float* out, long long out_elems, int nblocks, int it
 /*
  * fa_probe_hbm_read -- a streaming-read bandwidth probe.
  *
- * Reads every byte of `src` once with 16-byte loads spread over `nblocks` workgroups of 256
- * threads (grid-stride, four loads in flight per lane) and writes one XOR checksum per thread.
+ * Reads every byte of `src` once with nontemporal 16-byte loads: workgroup b of `nblocks` (256
+ * threads) reads the b-th of nblocks contiguous chunks, eight loads in flight per lane, and every
+ * thread writes one XOR checksum.
  *   src        device buffer of `bytes` bytes, 16-byte aligned; bytes a positive multiple of 16.
  *   out        device buffer of out_elems uint32 values, at least nblocks * 256 (FA_EINVAL otherwise).
  *   nblocks    1 .. 2^20.

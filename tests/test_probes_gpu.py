@@ -1,7 +1,8 @@
 """The measurement probes of include/fa_probe.h on the GPU (through the C ABI via the package binding).
 
-The streaming-read probe must read every 16-byte chunk of its buffer exactly once: its per-thread XOR
-checksums are recomputed on the host from the grid-stride assignment. The matrix-core probes (bf16 and
+The streaming-read probe must read every 16-byte word of its buffer exactly once: its per-thread XOR
+checksums are recomputed on the host from the assignment (workgroup b takes the b-th of nblocks
+contiguous chunks, thread t the words of its chunk at offsets t, t + 256, ...). The matrix-core probes (bf16 and
 fp32) must produce finite checksums that are identical in every workgroup (each computes the same
 products); the fp32 one is also compared with its closed form.
 """
@@ -17,7 +18,7 @@ if torch.cuda.is_available():
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("n16,nblocks", [(64 * 256 * 4 * 3 + 37, 64), (1000, 8), (256, 1)])
+@pytest.mark.parametrize("n16,nblocks", [(64 * 256 * 4 * 3 + 37, 64), (1000, 8), (256, 1), (256 * 8 * 5 + 3, 2)])
 def test_read_probe_reads_every_chunk_once(n16, nblocks):
     g = torch.Generator(device=DEV)
     g.manual_seed(n16)
@@ -28,10 +29,11 @@ def test_read_probe_reads_every_chunk_once(n16, nblocks):
     assert nbytes == n16 * 16
     chunks = buf.cpu().numpy().view(np.uint32).reshape(n16, 4)
     per_chunk = np.bitwise_xor.reduce(chunks, axis=1)
-    stride = nblocks * 256
-    expect = np.zeros(stride, dtype=np.uint32)
-    idx = np.arange(n16)
-    np.bitwise_xor.at(expect, idx % stride, per_chunk)
+    expect = np.zeros(nblocks * 256, dtype=np.uint32)
+    for b in range(nblocks):
+        beg, end = n16 * b // nblocks, n16 * (b + 1) // nblocks
+        idx = np.arange(beg, end)
+        np.bitwise_xor.at(expect, b * 256 + (idx - beg) % 256, per_chunk[beg:end])
     assert np.array_equal(out.cpu().numpy().view(np.uint32), expect)
 
 
