@@ -24,8 +24,11 @@
 // true maximum, so the partial states are the same (m, l, o) as the plain recurrence gives, up to
 // rounding. With one key per group step it also loads each step's K and V words one step ahead.
 //
-// K and V are read once, so their loads are nontemporal: 1415 -> 1258 us on B=16, H=32,
-// Nk=32768, d=128 split 16 ways (6.07 -> 6.83 TB/s of K and V), 369 -> 342 us with 8 K/V heads.
+// K and V are streamed with nontemporal loads: 1415 -> 1258 us on B=16, H=32, Nk=32768, d=128 split
+// 16 ways (6.07 -> 6.83 TB/s of K and V), 369 -> 342 us with 8 K/V heads. decode_rows_kernel always
+// uses them (its workgroups that share a K/V head read it at the same pace: 16 rows of a head, 314 ->
+// 286 us); decode_kernel only when each K/V head has one row (its causal rows read a shared K/V at
+// different times, and the hint made them slower).
 
 #include <type_traits>
 
@@ -64,6 +67,12 @@ __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[N
   }
 }
 
+// 16 bytes of a K or V row, nontemporal (streamed).
+template <typename T>
+__device__ __forceinline__ u32x4_t stream_u32x4(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out(void* base, size_t elem, int out_dtype, float x) {
   if (out_dtype == kF32) static_cast<float*>(base)[elem] = x;
@@ -71,7 +80,7 @@ __device__ __forceinline__ void store_out(void* base, size_t elem, int out_dtype
   else static_cast<_Float16*>(base)[elem] = (_Float16)x;
 }
 
-template <int D, typename T, int U>
+template <int D, typename T, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
   constexpr int NG = kGroups;
   constexpr int DL = D / 16;  // columns per lane
@@ -110,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int key = base + u;
       if (key < kend) {
-        load_row<T, DL, true>(K + (size_t)key * D, kx[u]);
-        load_row<T, DL, true>(V + (size_t)key * D, vx[u]);
+        load_row<T, DL, NT>(K + (size_t)key * D, kx[u]);
+        load_row<T, DL, NT>(V + (size_t)key * D, vx[u]);
       } else {
 #pragma unroll
         for (int c = 0; c < DL; ++c) kx[u][c] = vx[u][c] = 0.f;
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
   if constexpr (U == 1 && DL == 8) {
     const int key = kbeg + g;
     if (key < kend) {
-      kn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(K + (size_t)key * D));
-      vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(V + (size_t)key * D));
+      kn = stream_u32x4(K + (size_t)key * D);
+      vn = stream_u32x4(V + (size_t)key * D);
     }
   }
   for (int base = kbeg + g * U; base < kend; base += kGroups * U) {
@@ -261,8 +270,8 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(FwdArgs a) {
       const u32x4_t kc = kn, vc = vn;
       const int nk = base + kGroups;
       if (nk < kend) {
-        kn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(K + (size_t)nk * D));
-        vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(V + (size_t)nk * D));
+        kn = stream_u32x4(K + (size_t)nk * D);
+        vn = stream_u32x4(V + (size_t)nk * D);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -457,8 +466,13 @@ hipError_t launch_typed(const FwdArgs& a, hipStream_t s) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<D, T, U>), dim3((unsigned)nwg), dim3(kThreads),
-                         kargs, 0, s);
+  // nontemporal K / V loads when each K/V head is read by one workgroup per range; the rows of a
+  // causal launch share theirs at different times, and the hint made them slower (441 vs 317 us at
+  // B=4, H=8, Nq=4, Nk=8192)
+  const bool nt = a.Nq == 1 && a.H == a.H_kv;
+  const void* k = nt ? reinterpret_cast<const void*>(&decode_kernel<D, T, U, true>)
+                     : reinterpret_cast<const void*>(&decode_kernel<D, T, U, false>);
+  return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreads), kargs, 0, s);
 }
 
 }  // namespace

@@ -625,12 +625,14 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // Lane j of a group owns columns r * 4 * LPK + 4 j + [0, 4) for r < CPL / 4, so one 16-byte load
 // instruction of the wave covers whole contiguous row segments.
-template <int D>
+// NT: nontemporal loads (a stream only this workgroup reads).
+template <int D, bool NT = false>
 __device__ __forceinline__ void load_key_cols(const float* __restrict__ row, int j, float (&x)[F32RowCfg<D>::CPL]) {
   typedef F32RowCfg<D> C;
 #pragma unroll
   for (int r = 0; r < C::CPL / 4; ++r) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + r * 4 * C::LPK + 4 * j);
+    const f32x4_t* p = reinterpret_cast<const f32x4_t*>(row + r * 4 * C::LPK + 4 * j);
+    const f32x4_t v = NT ? __builtin_nontemporal_load(p) : *p;
     x[4 * r] = v[0];
     x[4 * r + 1] = v[1];
     x[4 * r + 2] = v[2];
@@ -638,7 +640,7 @@ __device__ __forceinline__ void load_key_cols(const float* __restrict__ row, int
   }
 }
 
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(kThreadsRows) void fwd_f32_rows_kernel(FwdArgs a) {
   typedef F32RowCfg<D> C;
   constexpr int CPL = C::CPL, LPK = C::LPK, G = C::G, NW = C::NW, P = C::P;
@@ -687,8 +689,8 @@ __global__ __launch_bounds__(kThreadsRows) void fwd_f32_rows_kernel(FwdArgs a) {
   // rows past kend repeat row kend - 1 (their keys take no part)
   auto load_step = [&](int i, float (&kx)[CPL], float (&vx)[CPL]) {
     const size_t key = (size_t)min(key_at(i), kend - 1);
-    load_key_cols<D>(K + key * D, j, kx);
-    load_key_cols<D>(V + key * D, j, vx);
+    load_key_cols<D, NT>(K + key * D, j, kx);
+    load_key_cols<D, NT>(V + key * D, j, vx);
   };
 #pragma unroll
   for (int p = 0; p < P; ++p)
@@ -846,8 +848,16 @@ hipError_t launch_fwd_f32_rows(const FwdArgs& a, int d, hipStream_t s) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  const void* k = d == 64 ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<64>)
-                : d == 128 ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<128>) : nullptr;
+  // K and V stream nontemporally when each K/V head is read by one workgroup per key range (one
+  // query row per K/V head: B=4, H=64, Nk=4096 one-query rows 96.7 -> 83.3 us at d = 64); with
+  // several rows per K/V head the hint evicts lines the other rows' workgroups still read
+  // (16 rows x 4 heads x 8192 keys: 49 -> 91 us), so those keep plain loads.
+  const bool nt = a.Nq == 1 && a.H == a.H_kv;
+  const void* k = d == 64 ? (nt ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<64, true>)
+                                : reinterpret_cast<const void*>(&fwd_f32_rows_kernel<64, false>))
+                : d == 128 ? (nt ? reinterpret_cast<const void*>(&fwd_f32_rows_kernel<128, true>)
+                                 : reinterpret_cast<const void*>(&fwd_f32_rows_kernel<128, false>))
+                           : nullptr;
   if (!k) return hipErrorInvalidValue;
   return hipLaunchKernel(k, dim3((unsigned)nwg), dim3(kThreadsRows), kargs, 0, s);
 }
