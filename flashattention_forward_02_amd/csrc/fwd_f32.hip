@@ -598,7 +598,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_mfma_kernel(FwdArgs a, int n_
 // round trips, not arithmetic. So the roles of rows and keys swap inside a wave: the wave holds
 // the one query row, and each group of LPK lanes (CPL columns each) takes a different key, so a
 // key costs its group CPL FMAs, a short exchange and one expf. K and V go straight into registers,
-// P steps ahead of their use, in 16 waves: about 256 KiB in flight per workgroup. Step i of wave
+// P steps ahead of their use, in 8 waves: about 128 KiB in flight per workgroup. Step i of wave
 // w covers keys kbeg + (i * NW + w) * G + [0, G), so the waves walk the range together. Each group
 // keeps its own (m, l, acc), summed plainly over 8 steps and then added with compensation; the
 // groups of a wave are merged, then the waves (all compensated).
@@ -607,7 +607,7 @@ struct F32RowCfg {
   static constexpr int CPL = 8;           // columns per lane
   static constexpr int LPK = D / CPL;     // lanes per key: 8 (d = 64) or 16 (d = 128)
   static constexpr int G = 64 / LPK;      // keys per wave step
-  static constexpr int NW = 16;           // waves per workgroup
+  static constexpr int NW = 8;            // waves per workgroup (16: single head 7.6 -> 6.5 us with 8)
   static constexpr int P = 4;             // steps in flight per wave
 };
 constexpr int kThreadsRows = F32RowCfg<64>::NW * 64;
