@@ -103,12 +103,13 @@ fa::FwdArgs make_args(const void* q, const void* k, const void* v, int B, int H,
 
 // fp32: the one-workgroup-per-row kernel takes every call with at most 16 query rows, and also
 // small calls with more: it spreads the rows over the compute units, where a small launch of the
-// tiled kernels leaves most of them idle. Measured faster up to 256 rows per launch at d = 64
-// (B=H=1, N=256: 9.2 -> 8.3 us per call; 256 queries x 2048 keys: 27.7 -> 17.1 us) and up to 1024
-// at d = 128, where the tiled kernel is the VALU one (256 x 1024: 73 -> 16 us); slower beyond.
+// tiled kernels leaves most of them idle. Measured faster up to 512 rows per launch at d = 64
+// (B=H=1, N=256: 9.2 -> 6.4 us per call; B=1, H=2, N=256: 9.2 -> 8.1; 512 queries x 1024 keys:
+// 17.4 -> 15.1) and up to 1024 at d = 128, where the tiled kernel is the VALU one (4 heads of
+// 256 x 1024: 74 -> 42 us); slower beyond (1024 rows at d = 64: 9.3 -> 14.0 us).
 bool f32_by_rows(const fa::FwdArgs& a, int d) {
   const long long rows = (long long)a.B * a.H * a.Nq * a.num_splits;
-  return a.Nq <= fa::kDecodeMaxNq || rows <= (d == 64 ? 256 : 1024);
+  return a.Nq <= fa::kDecodeMaxNq || rows <= (d == 64 ? 512 : 1024);
 }
 
 fa_status launched(const char* fn, hipError_t e) {

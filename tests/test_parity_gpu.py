@@ -63,8 +63,8 @@ SMALL = [
 
 # fp32 launches of at most 256 rows (d = 64) or 1024 (d = 128) run one workgroup per row, larger
 # ones the tiled kernels: both sides of each limit, with and without the mask and the statistics.
-F32_LIMITS = [(1, 1, 256, 300, 64), (1, 1, 257, 300, 64), (1, 4, 256, 300, 128), (1, 4, 257, 300, 128),
-              (2, 2, 64, 129, 64), (1, 3, 100, 1000, 64)]
+F32_LIMITS = [(1, 1, 512, 600, 64), (1, 1, 513, 600, 64), (1, 4, 256, 300, 128), (1, 4, 257, 300, 128),
+              (2, 2, 128, 129, 64), (2, 2, 129, 129, 64), (1, 3, 100, 1000, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
