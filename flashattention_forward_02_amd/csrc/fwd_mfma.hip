@@ -679,9 +679,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdArgs a, int n_
       phase_valu_full(t, false);
     }
     if constexpr (CAUSAL) {
-      for (int t = n_plain > 1 ? n_plain : 1; t < T_; ++t) {
+      // (d = 64, sum-checked) a wave whose rows saw no key of tile t - 1 sees none of the later
+      // tiles either: it leaves the loop (its PV of a zero P and its unused S are skipped) and
+      // only takes part in the loads, group A's V staging and the barriers, so the other wave of
+      // its SIMD has the matrix core and the VALU to itself on the last diagonal tiles (causal
+      // workload 148.6 -> 146.3 us). Its P is already 0, so the final PV adds nothing.
+      int t = n_plain > 1 ? n_plain : 1;
+      for (; t < T_ && !(STAGE && FAST && wave_masked(t - 1)); ++t) {
         phase_mfma(t, true, true);
         phase_valu_masked(t, false);
+      }
+      if constexpr (STAGE && FAST) {
+        for (; t < T_; ++t) {
+          if (group_a && t + 1 < T_) {
+            load_tile2<D, T, true>(K, lds_k[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane, koff);
+            load_tile2<D, T, false>(V, lds_v[(t + 1) & 1], kbeg + (t + 1) * kBC, kend, gw, lane, voff);
+          }
+          if (!group_a) __syncthreads();
+          valu_prologue(t);
+          if (group_a) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+          }
+        }
       }
     } else if (n_plain < T_ && T_ > 1) {
       phase_mfma(T_ - 1, true, true);
