@@ -256,6 +256,51 @@ def test_no_device_allocation_and_no_nxn_buffer():
     assert abs(free1 - free0) < 64 * 2 ** 20, (free0, free1)
 
 
+@pytest.mark.parametrize("path", ["fp32_fwd", "split_merge", "lse_bwd"])
+def test_no_device_allocation_other_paths(path):
+    """The fp32 forward, the split-KV states with their merge, and the forward-with-lse plus backward
+    allocate nothing either: with every output and workspace allocated up front, free device memory
+    and torch's allocation count are unchanged across the calls."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2)
+    if path == "fp32_fwd":
+        q = torch.randn((1, 1, 4096, 64), device=DEV, generator=g)
+        k = torch.randn((1, 1, 4096, 64), device=DEV, generator=g)
+        v = torch.randn((1, 1, 4096, 64), device=DEV, generator=g)
+        o = torch.empty_like(q)
+        run = lambda: fa.fwd(q, k, v, out=o)
+    elif path == "split_merge":
+        B, H, Nk, d, S = 4, 8, 8192, 128, 16
+        q = torch.randn((B, H, 1, d), device=DEV, generator=g).to(torch.bfloat16)
+        k = torch.randn((B, H, Nk, d), device=DEV, generator=g).to(torch.bfloat16)
+        v = torch.randn((B, H, Nk, d), device=DEV, generator=g).to(torch.bfloat16)
+        pm = torch.empty((S, B, H, 1), device=DEV)
+        pl = torch.empty_like(pm)
+        po = torch.empty((S, B, H, 1, d), device=DEV)
+        o = torch.empty((B, H, 1, d), device=DEV)
+        order = list(range(S))[::-1]
+
+        def run():
+            fa.fwd_split(q, k, v, S, workspace=(pm, pl, po))
+            fa.merge_states(pm, pl, po, order=order, out=o)
+    else:
+        B, H, N, d = 2, 4, 1024, 64
+        q, k, v, dout = (torch.randn((B, H, N, d), device=DEV, generator=g).to(torch.bfloat16) for _ in range(4))
+        o, lse = fa.fwd_lse(q, k, v)
+        grads = (torch.empty((B, H, N, d), device=DEV), torch.empty((B, H, N, d), device=DEV),
+                 torch.empty((B, H, N, d), device=DEV), torch.empty((B, H, N), device=DEV))
+        run = lambda: fa.bwd(q, k, v, o, dout, lse, out=grads)
+    run()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    run()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0, path
+    assert abs(free1 - free0) < 64 * 2 ** 20, (path, free0, free1)
+
+
 # ---------------------------------------------------------------------------------------------
 # the workloads
 # ---------------------------------------------------------------------------------------------
